@@ -1,0 +1,201 @@
+"""Plain, slow CPU oracle for the AQLM quantized linear layer y = W x.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import or call anything here.  It shares
+no code with the HIP library and imports nothing from it; both sides receive
+the same arrays from the seeded input generators.
+
+Sources (cited by page title and section):
+
+* "The AQLM Quantization Algorithm, Explained", section "What is Multi-Codebook
+  Quantization (MCQ)?": a row of W (shape d_out x d_in, W.X convention) is cut
+  into groups of g consecutive inputs; each group is approximated by the sum
+  of M codewords, one from each of M codebooks of 2^B codewords of size g held
+  at 16-bit precision; a group stores M indices of B bits; every output
+  channel carries a learned scale.  Figure 2 (dequantization): the selected
+  codewords are summed, then scaled, giving half-precision weights that the
+  matrix product consumes.
+* Same page, section "Memory footprint of AQLM-quantized models": the stored
+  items are M codebooks of 2^B fp16 codewords of size g, d_out fp16 scales and
+  M codes of B bits for each of the d_out*d_in/g groups; the average bits per
+  parameter is taken per weight matrix.  The formula itself did not survive
+  text extraction, so ``bits_per_weight`` re-derives it from those three
+  listed items.
+* Same page, section "Key AQLM quantization parameters": when the code term
+  dominates, bits per parameter is about B*M/g.
+
+Readings where the pages are silent (each one listed in the design doc):
+
+* group j of row i covers columns [j*g, (j+1)*g); codes are stored
+  ``[d_out][d_in/g][M]``; codebooks ``[M][2^B][g]``; scales ``[d_out]``;
+* a B=16 code held in an int16 is the bit pattern read as unsigned 0..65535;
+  a B=8 code held in a uint8 is its value;
+* the codewords are summed in fp32, codebook 0 first then m ascending, the
+  running sum starting from codebook 0's codeword (not from +0.0), then
+  multiplied by the fp32 scale; the fp16 weight is that fp32 value rounded to
+  nearest-even with subnormals kept;
+* the reference product uses the fp32 decoded weights widened to float64.
+
+Every function here is pinned by ``tests/test_oracle.py`` against closed
+forms, brute force on one-hot codebooks and facts the pages print.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# (M, B, g) triples the library accepts: 1x16 and 2x8 at g = 8
+# ("Key AQLM quantization parameters": XBit-MxB naming, e.g. 2Bit-1x16).
+SUPPORTED_SCHEMES = ((1, 16, 8), (2, 8, 8))
+
+
+def _check_layer(codes, codebooks, scales):
+    """Shape and dtype checks for one quantized layer; returns (M, B, g, out, in)."""
+    if codebooks.dtype != np.float16 or codebooks.ndim != 3:
+        raise ValueError("codebooks must be float16 [M][2^B][g]")
+    M, K, g = codebooks.shape
+    B = int(round(math.log2(K))) if K > 0 else -1
+    if K <= 0 or (1 << B) != K:
+        raise ValueError("codebook size must be a power of two")
+    if codes.ndim != 3 or codes.shape[2] != M:
+        raise ValueError("codes must be [out][in/g][M]")
+    if B <= 8:
+        if codes.dtype != np.uint8:
+            raise ValueError("B <= 8 codes must be uint8")
+    elif B <= 16:
+        if codes.dtype not in (np.int16, np.uint16):
+            raise ValueError("B = 16 codes must be int16 (bit pattern) or uint16")
+    else:
+        raise ValueError("B > 16 not representable")
+    out, G, _ = codes.shape
+    if scales.dtype != np.float16 or scales.shape != (out,):
+        raise ValueError("scales must be float16 [out]")
+    return M, B, g, out, G * g
+
+
+def codes_to_index(codes: np.ndarray) -> np.ndarray:
+    """Codeword index of every stored code, as int64.
+
+    A code is the position of the selected codeword inside its codebook
+    (MCQ section: the one-hot vector is stored as its index).  uint8 codes are
+    their value; int16 codes are their 16-bit pattern read as unsigned.
+    """
+    if codes.dtype == np.uint8 or codes.dtype == np.uint16:
+        return codes.astype(np.int64)
+    if codes.dtype == np.int16:
+        return codes.view(np.uint16).astype(np.int64)
+    raise ValueError(f"unsupported code dtype {codes.dtype}")
+
+
+def decode_fp32(codes, codebooks, scales, rows=None) -> np.ndarray:
+    """Dequantized weights in fp32, shape [out][in] (or [len(rows)][in]).
+
+    Figure 2 of the MCQ section: look up one codeword per codebook, sum them
+    (fp32, codebook 0 first, m ascending), then multiply by the row's scale.
+    """
+    M, B, g, out, n_in = _check_layer(codes, codebooks, scales)
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        codes = codes[rows]
+        scales = scales[rows]
+    idx = codes_to_index(codes)                      # [r][G][M]
+    acc = codebooks[0][idx[:, :, 0]].astype(np.float32)          # [r][G][g]
+    for m in range(1, M):
+        acc = acc + codebooks[m][idx[:, :, m]].astype(np.float32)
+    w = acc * scales.astype(np.float32)[:, None, None]
+    return w.reshape(w.shape[0], n_in)
+
+
+def decode_fp16(codes, codebooks, scales, rows=None) -> np.ndarray:
+    """fp16 weights: the fp32 decode rounded to nearest-even (subnormals kept)."""
+    return decode_fp32(codes, codebooks, scales, rows).astype(np.float16)
+
+
+def decode_loop(codes, codebooks, scales) -> np.ndarray:
+    """Same decode as ``decode_fp32``, written as explicit loops (tiny layers only).
+
+    Independent second reading of the MCQ-section definition, used to pin the
+    vectorised gather.  Each sum and product is rounded to fp32 one operation
+    at a time.
+    """
+    M, B, g, out, n_in = _check_layer(codes, codebooks, scales)
+    G = n_in // g
+    w = np.zeros((out, n_in), dtype=np.float32)
+    f32 = np.float32
+    for i in range(out):
+        s = f32(scales[i])
+        for j in range(G):
+            for t in range(g):
+                acc = None
+                for m in range(M):
+                    c = int(codes[i, j, m])
+                    if codes.dtype == np.int16 and c < 0:
+                        c += 1 << 16
+                    v = f32(codebooks[m, c, t])
+                    acc = v if acc is None else f32(acc + v)
+                w[i, j * g + t] = f32(acc * s)
+    return w
+
+
+def linear_ref_f64(codes, codebooks, scales, x) -> np.ndarray:
+    """y[b][i] = sum_k W[i][k] * x[b][k] in float64, W from ``decode_fp32``.
+
+    The matrix product on dequantized weights that Figure 2 of the MCQ
+    section feeds; x is [T][in] fp16, the result [T][out] float64.
+    """
+    w = decode_fp32(codes, codebooks, scales)
+    x = np.asarray(x)
+    if x.ndim != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [T][in]")
+    return (w.astype(np.float64) @ x.astype(np.float64).T).T
+
+
+def linear_ref_rows_f64(codes, codebooks, scales, x, rows) -> np.ndarray:
+    """Columns ``rows`` of the reference output: y[:, rows], float64 [T][len(rows)].
+
+    For full-size layers where decoding all of W on the host would be slow.
+    """
+    w = decode_fp32(codes, codebooks, scales, rows=rows)
+    return (w.astype(np.float64) @ np.asarray(x).astype(np.float64).T).T
+
+
+def bits_per_weight_terms(M, B, g, d_out, d_in):
+    """Average bits per parameter of one weight matrix, split by stored item.
+
+    "Memory footprint of AQLM-quantized models": codes (M codes of B bits for
+    each of d_out*d_in/g groups), codebooks (M * 2^B codewords of g fp16
+    values) and scales (d_out fp16 values), each divided by d_out*d_in.
+    """
+    n = d_out * d_in
+    codes = M * B * (d_out * d_in // g) / n
+    codebooks = M * (2 ** B) * g * 16 / n
+    scales = d_out * 16 / n
+    return {"codes": codes, "codebooks": codebooks, "scales": scales,
+            "total": codes + codebooks + scales}
+
+
+def bits_per_weight(M, B, g, d_out, d_in) -> float:
+    return bits_per_weight_terms(M, B, g, d_out, d_in)["total"]
+
+
+def parity_errors(y, y_ref):
+    """(relative L2 error, max abs error, max |y_ref|) in float64 over all outputs."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    if y.shape != y_ref.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {y_ref.shape}")
+    diff = y - y_ref
+    ref_norm = float(np.linalg.norm(y_ref))
+    rel = float(np.linalg.norm(diff)) / ref_norm if ref_norm > 0 else float(np.linalg.norm(diff))
+    return rel, float(np.max(np.abs(diff))) if diff.size else 0.0, float(np.max(np.abs(y_ref))) if y_ref.size else 0.0
+
+
+# GEMV/GEMM acceptance: relative L2 <= 1e-3 and max abs <= 1e-2 * max|y_ref|.
+REL_L2_TOL = 1e-3
+MAX_ABS_FRAC = 1e-2
+
+
+def within_tolerance(y, y_ref):
+    rel, mx, ref_max = parity_errors(y, y_ref)
+    return rel <= REL_L2_TOL and mx <= MAX_ABS_FRAC * ref_max

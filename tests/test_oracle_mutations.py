@@ -1,0 +1,50 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins in test_oracle.py catch every one of them."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "drop_second_codebook": (
+        "for m in range(1, M):\n        acc = acc + codebooks[m][idx[:, :, m]].astype(np.float32)", "pass"),
+    "int16_codes_signed": (
+        "return codes.view(np.uint16).astype(np.int64)", "return codes.astype(np.int64)"),
+    "sum_starts_at_plus_zero": (
+        "acc = codebooks[0][idx[:, :, 0]].astype(np.float32)          # [r][G][g]\n    for m in range(1, M):",
+        "acc = np.zeros(idx.shape[:2] + (g,), np.float32)\n    for m in range(0, M):"),
+    "scale_off_by_rounding": (
+        "w = acc * scales.astype(np.float32)[:, None, None]",
+        "w = acc * (scales.astype(np.float32)[:, None, None] * np.float32(1.0001))"),
+    "codes_m_swapped": (
+        "acc = codebooks[0][idx[:, :, 0]]", "acc = codebooks[0][idx[:, :, M - 1]]"),
+    "column_order_t_major": (
+        "return w.reshape(w.shape[0], n_in)", "return w.transpose(0, 2, 1).reshape(w.shape[0], n_in)"),
+    "product_transposed": (
+        "return (w.astype(np.float64) @ x.astype(np.float64).T).T",
+        "return (w.astype(np.float64) @ x.astype(np.float64).T)"),
+    "fp16_running_sum": (
+        "acc = acc + codebooks[m][idx[:, :, m]].astype(np.float32)",
+        "acc = (acc.astype(np.float16) + codebooks[m][idx[:, :, m]]).astype(np.float32)"),
+    "bpw_scale_32bit": ("scales = d_out * 16 / n", "scales = d_out * 32 / n"),
+    "bpw_one_codebook": ("codebooks = M * (2 ** B) * g * 16 / n", "codebooks = (2 ** B) * g * 16 / n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    before, after = MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "aqlm_oracle.py")).read()
+    assert before in src, f"mutation site for {name} not found"
+    dst = tmp_path / "oracle"
+    shutil.copytree(os.path.join(ROOT, "oracle"), dst, ignore=shutil.ignore_patterns("__pycache__"))
+    (dst / "aqlm_oracle.py").write_text(src.replace(before, after))
+    env = dict(os.environ, AQLM_ORACLE_MUTANT_DIR=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       capture_output=True, text=True, env=env, cwd=ROOT, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived:\n{r.stdout[-2000:]}"
