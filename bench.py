@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Benchmark of the AQLM 2-bit quantized linear layer on one MI355X.
+
+Headline workload: the seven projections of one Llama-2-7B decoder block
+(q, k, v, o 4096x4096; gate, up 11008x4096; down 4096x11008) as AQLM 1x16
+(one 65536-entry fp16 codebook, int16 codes, g = 8) decode-phase GEMVs at
+batch 1.  One step runs all seven layers once.  The reported value is the
+achieved HBM bandwidth over the counted bytes (codes + scales + activations
++ outputs), with inputs resident in HBM and rotated over enough distinct
+buffer sets to defeat the 256 MB last-level cache.
+
+Also measured in the same run (reported under "breakdown", not in value):
+2x8 GEMV at batch 1/4/16 on the same block, the Llama-2-70B 1x16 layers at
+batch 1, the 2048-token prefill GEMM on the 7B shapes (both schemes) and the
+standalone decode kernel.  The CPU oracle is timed on the host on one of each
+7B layer shape.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
+LLC_BYTES = 256 << 20          # MI355X Infinity Cache
+
+BLOCK_7B = ((4096, 4096),) * 4 + ((11008, 4096),) * 2 + ((4096, 11008),)
+SHAPES_7B = ((4096, 4096), (11008, 4096), (4096, 11008))
+SHAPES_70B = ((8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672))
+SCHEMES = {"2x8": (2, 8, 8, 0.05), "1x16": (1, 16, 8, 0.02)}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemv_bytes(out, n_in, batch):
+    """Counted bytes of one GEMV: codes (2 bits/weight) + scales + x + y."""
+    return out * n_in // 4 + 2 * out + 2 * n_in * batch + 2 * out * batch
+
+
+# ----------------------------------------------------------------------------
+# Synthetic layers on the GPU (seeded torch generator; same distributions as
+# extreme_weight_quantization_amd.synth, drawn on the device for speed).
+
+
+def make_codebooks(torch, scheme, gen):
+    M, B, g, sigma = SCHEMES[scheme]
+    cb = torch.randn((M, 1 << B, g), generator=gen, device="cuda", dtype=torch.float32) * sigma
+    return cb.half()
+
+
+def make_codes(torch, scheme, out, n_in, gen):
+    M, B, g, _ = SCHEMES[scheme]
+    if B == 8:
+        return torch.randint(0, 256, (out, n_in // g, M), generator=gen, device="cuda", dtype=torch.uint8)
+    return torch.randint(-32768, 32768, (out, n_in // g, M), generator=gen, device="cuda", dtype=torch.int16)
+
+
+def make_scales(torch, out, gen):
+    return (torch.rand(out, generator=gen, device="cuda") + 0.5).half()
+
+
+def make_x(torch, batch, n_in, gen):
+    return torch.randn((batch, n_in), generator=gen, device="cuda").half()
+
+
+class LayerSet:
+    """n_sets distinct copies of codes+scales (+x, y) for a list of layer shapes."""
+
+    def __init__(self, torch, scheme, shapes, batch, n_sets, seed=0):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
+        self.scheme, self.shapes, self.batch = scheme, shapes, batch
+        self.cb = make_codebooks(torch, scheme, gen)
+        self.sets = []
+        for _ in range(n_sets):
+            layers = []
+            for out, n_in in shapes:
+                layers.append((make_codes(torch, scheme, out, n_in, gen), make_scales(torch, out, gen),
+                               make_x(torch, batch, n_in, gen),
+                               torch.empty((batch, out), dtype=torch.float16, device="cuda")))
+            self.sets.append(layers)
+        self.bytes_per_step = sum(gemv_bytes(o, i, batch) for o, i in shapes)
+
+
+def sets_needed(shapes, batch, min_bytes=4 * LLC_BYTES, cap=64):
+    per = sum(gemv_bytes(o, i, batch) for o, i in shapes)
+    return max(2, min(cap, -(-min_bytes // per)))
+
+
+# ----------------------------------------------------------------------------
+
+
+def capture(torch, launches):
+    """A HIP graph of the given launch closures (run once eagerly first)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in launches:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in launches:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_us(torch, graph, reps=1):
+    """Wall time on the device of `reps` replays of `graph`, in microseconds (HIP events)."""
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3
+
+
+def gemv_launches(E, ls, k0, n_steps, only=None):
+    out = []
+    for k in range(k0, k0 + n_steps):
+        for li, (codes, s, x, y) in enumerate(ls.sets[k % len(ls.sets)]):
+            if only is None or ls.shapes[li] == only:
+                out.append(lambda c=codes, s=s, x=x, y=y: E.aqlm_linear_gemv(c, ls.cb, s, x, y))
+    return out
+
+
+def time_gemv(torch, E, ls: LayerSet, steps, warmup):
+    """Times exactly `steps` passes over the layer list (rotating buffer sets).
+
+    The launches are captured in a HIP graph so that the device runs them
+    back to back; the timed region is one replay of that graph between two
+    HIP events.  Per-shape kernel durations come from graphs of back-to-back
+    launches of one shape.  Returns (ms per step, {shape: us per launch}).
+    """
+    g_warm = capture(torch, gemv_launches(E, ls, 0, max(1, warmup)))
+    g_main = capture(torch, gemv_launches(E, ls, warmup, steps))
+    replay_us(torch, g_warm)
+    ms_step = replay_us(torch, g_main) / steps / 1e3
+    per_shape = {}
+    for shape in dict.fromkeys(ls.shapes):
+        n = max(1, min(len(ls.sets), 64))
+        g = capture(torch, gemv_launches(E, ls, 0, n, only=shape))
+        count = n * ls.shapes.count(shape)
+        replay_us(torch, g)
+        per_shape[shape] = replay_us(torch, g, reps=4) / (4 * count)
+        del g
+    del g_warm, g_main
+    return ms_step, per_shape
+
+
+def time_calls(torch, launch, iters, warmup):
+    """Mean us per launch of `launch(i)` over `iters` back-to-back launches in a HIP graph."""
+    for i in range(warmup):
+        launch(i)
+    g = capture(torch, [lambda i=i: launch(i) for i in range(iters)])
+    replay_us(torch, g)
+    us = replay_us(torch, g, reps=3) / (3 * iters)
+    del g
+    return us
+
+
+def spot_check(torch, E, ls: LayerSet, rows_per_layer=32):
+    """Compares sampled outputs of set 0 with the CPU oracle (parity of the timed launches)."""
+    from oracle import aqlm_oracle as O
+    worst = 0.0
+    cb = ls.cb.cpu().numpy()
+    for (codes, s, x, y) in ls.sets[0]:
+        E.aqlm_linear_gemv(codes, ls.cb, s, x, y)
+        torch.cuda.synchronize()
+        out = codes.shape[0]
+        rows = np.unique(np.linspace(0, out - 1, rows_per_layer).astype(np.int64))
+        yr = O.linear_ref_rows_f64(codes.cpu().numpy(), cb, s.cpu().numpy(), x.cpu().numpy(), rows)
+        rel, mx, ref_max = O.parity_errors(y.cpu().numpy().astype(np.float64)[:, rows], yr)
+        if not (rel <= 1e-3 and mx <= 1e-2 * ref_max):
+            raise RuntimeError(f"parity check failed: rel {rel:.3e} max {mx:.3e}")
+        worst = max(worst, rel)
+    return worst
+
+
+def cpu_baseline(seconds_hint=True):
+    """The CPU oracle (decode in fp32, float64 product) on one of each 7B layer shape, 1x16, batch 1."""
+    from extreme_weight_quantization_amd import synth
+    from oracle import aqlm_oracle as O
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    nbytes = 0
+    elapsed = 0.0
+    for out, n_in in SHAPES_7B:
+        L = synth.make_layer("1x16", out, n_in, batch=1, seed=0)
+        t = time.perf_counter()
+        O.linear_ref_f64(L.codes, L.codebooks, L.scales, L.x)
+        elapsed += time.perf_counter() - t
+        nbytes += gemv_bytes(out, n_in, 1)
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "numpy oracle (fp32 decode + float64 product) on one 4096x4096, one 11008x4096 "
+                      f"and one 4096x11008 AQLM 1x16 layer at batch 1: {elapsed:.1f} s for "
+                      f"{nbytes / 1e6:.1f} MB counted bytes",
+            "us_per_layer": round(elapsed / 3 * 1e6, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only, no breakdown or CPU leg")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import extreme_weight_quantization_amd as E
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    E.load_library()
+    torch.cuda.init()
+    dev_name = torch.cuda.get_device_name(0)
+
+    # ---- headline: 7B block, 1x16, batch 1 ---------------------------------
+    n_sets = sets_needed(BLOCK_7B, 1)
+    ls = LayerSet(torch, "1x16", BLOCK_7B, 1, n_sets, seed=0)
+    worst = spot_check(torch, E, ls)
+    torch.cuda.synchronize()
+    ms_step, shape_us = time_gemv(torch, E, ls, args.steps, args.warmup)
+    value = ls.bytes_per_step / (ms_step * 1e-3) / 1e9
+    kern_us_step = sum(shape_us[sh] for sh in BLOCK_7B)
+    achieved = ls.bytes_per_step / (kern_us_step * 1e-6) / 1e9
+    per_shape = {f"{o}x{i}": {"us": round(us, 3), "GBps": round(gemv_bytes(o, i, 1) / (us * 1e-6) / 1e9, 1),
+                              "pct_hbm_peak": round(100 * gemv_bytes(o, i, 1) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+                 for (o, i), us in shape_us.items()}
+    del ls
+    torch.cuda.empty_cache()
+
+    breakdown = {"gemv_1x16_b1_7b": per_shape}
+    if not args.quick:
+        iters = max(20, args.steps // 2)
+        # 2x8 GEMV on the 7B block at batch 1, 4, 16
+        for b in (1, 4, 16):
+            ls2 = LayerSet(torch, "2x8", BLOCK_7B, b, sets_needed(BLOCK_7B, b), seed=1)
+            if b == 1:
+                spot_check(torch, E, ls2)
+            ms2, sh2 = time_gemv(torch, E, ls2, iters, 5)
+            k2 = sum(sh2[sh] for sh in BLOCK_7B)
+            breakdown[f"gemv_2x8_b{b}_7b_block"] = {
+                "us_per_layer": round(k2 / len(BLOCK_7B), 3),
+                "GBps_kernel": round(ls2.bytes_per_step / (k2 * 1e-6) / 1e9, 1),
+                "GBps_step": round(ls2.bytes_per_step / (ms2 * 1e-3) / 1e9, 1),
+                "per_shape": {f"{o}x{i}": {"us": round(us, 3),
+                                           "GBps": round(gemv_bytes(o, i, b) / (us * 1e-6) / 1e9, 1)}
+                              for (o, i), us in sh2.items()}}
+            del ls2
+            torch.cuda.empty_cache()
+        # 70B layers, 1x16, batch 1
+        r70 = {}
+        for shape in SHAPES_70B:
+            ls3 = LayerSet(torch, "1x16", (shape,), 1, sets_needed((shape,), 1, cap=16), seed=2)
+            _, sh3 = time_gemv(torch, E, ls3, iters, 5)
+            k3 = sh3[shape]
+            r70[f"{shape[0]}x{shape[1]}"] = {"us": round(k3, 3),
+                                             "GBps": round(ls3.bytes_per_step / (k3 * 1e-6) / 1e9, 1)}
+            del ls3
+            torch.cuda.empty_cache()
+        breakdown["gemv_1x16_b1_70b"] = r70
+        # prefill GEMM, 2048 tokens
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(3)
+        gm = {}
+        for scheme in ("2x8", "1x16"):
+            cb = make_codebooks(torch, scheme, gen)
+            for out, n_in in SHAPES_7B:
+                codes = make_codes(torch, scheme, out, n_in, gen)
+                s = make_scales(torch, out, gen)
+                x = make_x(torch, 2048, n_in, gen)
+                y = torch.empty((2048, out), dtype=torch.float16, device="cuda")
+                us = time_calls(torch, lambda i: E.aqlm_linear_gemm(codes, cb, s, x, y), 10, 2)
+                tf = 2.0 * 2048 * out * n_in / (us * 1e-6) / 1e12
+                gm[f"{scheme}_{out}x{n_in}"] = {"us": round(us, 1), "TFLOPs": round(tf, 1),
+                                                "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+                del codes, s, x, y
+            torch.cuda.empty_cache()
+        breakdown["gemm_prefill_2048"] = gm
+        # standalone decode, 4096x4096
+        dc = {}
+        for scheme in ("2x8", "1x16"):
+            cb = make_codebooks(torch, scheme, gen)
+            codes = make_codes(torch, scheme, 4096, 4096, gen)
+            s = make_scales(torch, 4096, gen)
+            w = torch.empty((4096, 4096), dtype=torch.float16, device="cuda")
+            us = time_calls(torch, lambda i: E.aqlm_linear_decode(codes, cb, s, w), 20, 3)
+            nbytes = 4096 * 4096 // 4 + 2 * 4096 + 2 * 4096 * 4096
+            dc[f"{scheme}_4096x4096"] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        breakdown["decode"] = dc
+
+    cpu = None if (args.quick or args.no_cpu) else cpu_baseline()
+
+    rec = {
+        "metric": "AQLM 2-bit linear us/layer + achieved HBM GB/s (% peak), 7B/70B shapes",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-2-7B decoder-block projections (q,k,v,o 4096x4096; gate,up 11008x4096; "
+                        "down 4096x11008) as AQLM 1x16 g8 decode GEMV, batch 1",
+            "scheme": "1x16", "group": 8, "batch": 1, "layers_per_step": len(BLOCK_7B),
+            "rotated_buffer_sets": n_sets, "parallelism": "single GPU",
+            "us_per_layer": round(ms_step * 1e3 / len(BLOCK_7B), 3),
+            "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "spot_check_rel_l2": worst,
+            "device": dev_name,
+        },
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_kernel<1x16>", "kernel_us_per_step": round(kern_us_step, 3),
+                     "method": "per-shape mean duration of back-to-back launches replayed from a HIP graph"},
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,6 +1,15 @@
 """AQLM 2-bit quantized linear layer for AMD Instinct MI355X (gfx950).
 
 The compute path is a C-ABI shared library of hand-written HIP kernels
-(``libaqlm.so``, declared in ``include/aqlm.h``); this package holds the thin
-ctypes binding to it and the seeded synthetic-input generators.
+(``libaqlm.so``, declared in ``include/aqlm.h``).  ``binding`` is the thin
+ctypes layer over it; ``synth`` draws seeded synthetic layers.  The library
+is loaded on first use and its absence is an error: there is no fallback.
 """
+from .binding import (  # noqa: F401
+    AqlmError,
+    aqlm_linear_decode,
+    aqlm_linear_gemm,
+    aqlm_linear_gemv,
+    load_library,
+    status_str,
+)

@@ -1,0 +1,153 @@
+"""ctypes binding of libaqlm.so (declared in include/aqlm.h).
+
+Argument marshalling only: tensors are checked for device, dtype and
+contiguity, their data pointers and sizes are handed to the C ABI together
+with torch's current HIP stream, and status codes become exceptions.  Every
+step of the computation runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaqlm.so")
+
+AQLM_OK, AQLM_ERR_NULL, AQLM_ERR_SHAPE, AQLM_ERR_SCHEME, AQLM_ERR_ALIGN, AQLM_ERR_HIP = range(6)
+EXPORTED = ("aqlm_linear_gemv", "aqlm_linear_gemm", "aqlm_linear_decode",
+            "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class AqlmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libaqlm.so once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m extreme_weight_quantization_amd.build`")
+        lib = ctypes.CDLL(path)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        for name in ("aqlm_linear_gemv", "aqlm_linear_gemm", "aqlm_linear_decode"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, i64, i64, i64, vp]
+            fn.restype = ci
+        lib.aqlm_status_str.argtypes = [ci]
+        lib.aqlm_status_str.restype = ctypes.c_char_p
+        lib.aqlm_last_hip_error.argtypes = []
+        lib.aqlm_last_hip_error.restype = ci
+        lib.aqlm_version.argtypes = []
+        lib.aqlm_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().aqlm_status_str(int(status)).decode()
+
+
+def _check(status: int):
+    if status == AQLM_OK:
+        return
+    lib = load_library()
+    msg = lib.aqlm_status_str(status).decode()
+    if status == AQLM_ERR_HIP:
+        raise AqlmError(status, f"{msg} (hipError_t {lib.aqlm_last_hip_error()})")
+    err = AqlmError(status, msg)
+    raise ValueError(msg) from err
+
+
+def _scheme(codes: torch.Tensor, codebooks: torch.Tensor):
+    if codebooks.dim() != 3:
+        raise ValueError("codebooks must be [M][2^B][g]")
+    M, K, g = codebooks.shape
+    B = K.bit_length() - 1
+    return int(M), int(B), int(g)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensors(codes, codebooks, scales, x):
+    for name, t in (("codes", codes), ("codebooks", codebooks), ("scales", scales), ("x", x)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if codebooks.dtype != torch.float16 or scales.dtype != torch.float16:
+        raise ValueError("codebooks and scales must be float16")
+    if codes.dtype not in (torch.uint8, torch.int16):
+        raise ValueError("codes must be uint8 (B=8) or int16 (B=16)")
+    if x is not None and x.dtype != torch.float16:
+        raise ValueError("x must be float16")
+    if codes.dim() != 3:
+        raise ValueError("codes must be [out][in/g][M]")
+
+
+def _linear(fn_name, codes, codebooks, scales, x, y):
+    _check_tensors(codes, codebooks, scales, x)
+    M, B, g = _scheme(codes, codebooks)
+    out, G = int(codes.shape[0]), int(codes.shape[1])
+    n_in = G * g
+    if x.dim() != 2 or x.shape[1] != n_in:
+        raise ValueError(f"x must be [batch][{n_in}]")
+    batch = int(x.shape[0])
+    if y is None:
+        y = torch.empty((batch, out), dtype=torch.float16, device=x.device)
+    elif y.shape != (batch, out) or y.dtype != torch.float16 or not y.is_contiguous():
+        raise ValueError(f"y must be a contiguous float16 [{batch}][{out}] tensor")
+    fn = getattr(load_library(), fn_name)
+    _check(fn(_ptr(codes), _ptr(codebooks), _ptr(scales), _ptr(x), _ptr(y), M, B, g,
+              out, n_in, batch, _stream(x.device)))
+    return y
+
+
+def aqlm_linear_gemv(codes, codebooks, scales, x, y=None):
+    """y[b] = W x[b] for a decode batch of 1..16 rows of x (see aqlm.h)."""
+    return _linear("aqlm_linear_gemv", codes, codebooks, scales, x, y)
+
+
+def aqlm_linear_gemm(codes, codebooks, scales, x, y=None):
+    """Y = X W^T for a prefill batch of tokens (see aqlm.h)."""
+    return _linear("aqlm_linear_gemm", codes, codebooks, scales, x, y)
+
+
+def aqlm_linear_decode(codes, codebooks, scales, w=None):
+    """W16[out][in] = dequantized weights, bit-exact (see aqlm.h)."""
+    _check_tensors(codes, codebooks, scales, None)
+    M, B, g = _scheme(codes, codebooks)
+    out, G = int(codes.shape[0]), int(codes.shape[1])
+    if w is None:
+        w = torch.empty((out, G * g), dtype=torch.float16, device=codes.device)
+    elif w.shape != (out, G * g) or w.dtype != torch.float16 or not w.is_contiguous():
+        raise ValueError(f"w must be a contiguous float16 [{out}][{G * g}] tensor")
+    _check(load_library().aqlm_linear_decode(_ptr(codes), _ptr(codebooks), _ptr(scales), None,
+                                             _ptr(w), M, B, g, out, G * g, 0, _stream(codes.device)))
+    return w
+
+
+def raw_call(fn_name, codes, codebooks, scales, x, y, M, B, g, out, n_in, batch, stream=0) -> int:
+    """Call an entry point with raw integers/pointers and return its status (no checks)."""
+    fn = getattr(load_library(), fn_name)
+    return int(fn(ctypes.c_void_p(codes), ctypes.c_void_p(codebooks), ctypes.c_void_p(scales),
+                  ctypes.c_void_p(x), ctypes.c_void_p(y), M, B, g, out, n_in, batch,
+                  ctypes.c_void_p(stream)))

@@ -1,0 +1,128 @@
+// C ABI of libaqlm.so (declared in include/aqlm.h): argument validation on the
+// host, then dispatch to the HIP kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/aqlm.h"
+#include "aqlm_device.h"
+#include "aqlm_launch.h"
+
+namespace aqlm {
+
+namespace {
+thread_local int g_last_hip_error = 0;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+}  // namespace
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+enum class Op { kGemv, kGemm, kDecode };
+
+static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Host-side validation shared by the three entry points.  Returns AQLM_OK and
+// the scheme id, or an error status; touches no HIP state.
+static int validate(Op op, const void* codes, const void* codebooks, const void* scales,
+                    const void* x, const void* y, int M, int B, int g, int64_t out, int64_t in,
+                    int64_t batch, int* scheme, bool* empty) {
+    if (op == Op::kDecode && x != nullptr) return AQLM_ERR_NULL;
+    if (M == 1 && B == 16 && g == 8) *scheme = kScheme1x16;
+    else if (M == 2 && B == 8 && g == 8) *scheme = kScheme2x8;
+    else return AQLM_ERR_SCHEME;
+    if (out < 0 || in < 1 || in > AQLM_MAX_IN || (in % g) != 0) return AQLM_ERR_SHAPE;
+    if (out > (int64_t)INT32_MAX - 16) return AQLM_ERR_SHAPE;
+    if (op == Op::kGemv && (batch < 0 || batch > AQLM_GEMV_MAX_BATCH)) return AQLM_ERR_SHAPE;
+    if (op == Op::kGemm && (batch < 0 || batch > (int64_t)INT32_MAX - 256)) return AQLM_ERR_SHAPE;
+    if (op == Op::kDecode && (uint64_t)out * (uint64_t)(in / g) > (uint64_t)UINT32_MAX) return AQLM_ERR_SHAPE;
+    if (op == Op::kGemm) {
+        const uint64_t tiles = (uint64_t)((out + 127) / 128) * (uint64_t)((batch + 127) / 128);
+        if (tiles > (uint64_t)INT32_MAX) return AQLM_ERR_SHAPE;
+    }
+    // An empty problem reads and writes nothing: its (possibly NULL) pointers are not used.
+    *empty = (out == 0) || (op != Op::kDecode && batch == 0);
+    if (*empty) return AQLM_OK;
+    if (!codes || !codebooks || !scales || !y) return AQLM_ERR_NULL;
+    if (op != Op::kDecode && x == nullptr) return AQLM_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(codebooks, 16) || !aligned(y, 16) || !aligned(scales, 2))
+        return AQLM_ERR_ALIGN;
+    if (x && !aligned(x, 16)) return AQLM_ERR_ALIGN;
+    return AQLM_OK;
+}
+
+static int finish(hipError_t e) {
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return AQLM_ERR_HIP;
+    }
+    return AQLM_OK;
+}
+
+}  // namespace aqlm
+
+using namespace aqlm;
+
+extern "C" {
+
+int aqlm_linear_gemv(const void* codes, const void* codebooks, const void* scales, const void* x,
+                     void* y, int M, int B, int g, int64_t out, int64_t in, int64_t batch,
+                     void* stream) {
+    int scheme = 0;
+    bool empty = false;
+    const int st = validate(Op::kGemv, codes, codebooks, scales, x, y, M, B, g, out, in, batch, &scheme, &empty);
+    if (st != AQLM_OK || empty) return st;
+    return finish(launch_gemv(scheme, codes, codebooks, scales, x, y, out, in, batch,
+                              (hipStream_t)stream));
+}
+
+int aqlm_linear_gemm(const void* codes, const void* codebooks, const void* scales, const void* x,
+                     void* y, int M, int B, int g, int64_t out, int64_t in, int64_t batch,
+                     void* stream) {
+    int scheme = 0;
+    bool empty = false;
+    const int st = validate(Op::kGemm, codes, codebooks, scales, x, y, M, B, g, out, in, batch, &scheme, &empty);
+    if (st != AQLM_OK || empty) return st;
+    return finish(launch_gemm(scheme, codes, codebooks, scales, x, y, out, in, batch,
+                              (hipStream_t)stream));
+}
+
+int aqlm_linear_decode(const void* codes, const void* codebooks, const void* scales, const void* x,
+                       void* y, int M, int B, int g, int64_t out, int64_t in, int64_t batch,
+                       void* stream) {
+    (void)batch;
+    int scheme = 0;
+    bool empty = false;
+    const int st = validate(Op::kDecode, codes, codebooks, scales, x, y, M, B, g, out, in, 1, &scheme, &empty);
+    if (st != AQLM_OK || empty) return st;
+    return finish(launch_decode(scheme, codes, codebooks, scales, y, out, in, (hipStream_t)stream));
+}
+
+const char* aqlm_status_str(int status) {
+    switch (status) {
+        case AQLM_OK: return "AQLM_OK";
+        case AQLM_ERR_NULL: return "AQLM_ERR_NULL: a required pointer is NULL (decode takes x == NULL)";
+        case AQLM_ERR_SHAPE: return "AQLM_ERR_SHAPE: out/in/batch out of range or in % g != 0";
+        case AQLM_ERR_SCHEME: return "AQLM_ERR_SCHEME: (M, B, g) must be (1,16,8) or (2,8,8)";
+        case AQLM_ERR_ALIGN: return "AQLM_ERR_ALIGN: codes/codebooks/x/y need 16-byte, scales 2-byte alignment";
+        case AQLM_ERR_HIP: return "AQLM_ERR_HIP: HIP runtime error at launch (see aqlm_last_hip_error)";
+        default: return "unknown aqlm status";
+    }
+}
+
+int aqlm_last_hip_error(void) { return g_last_hip_error; }
+
+const char* aqlm_version(void) { return "0.1.0"; }
+
+}  // extern "C"

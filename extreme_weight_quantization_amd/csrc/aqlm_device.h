@@ -1,0 +1,42 @@
+// Device-side helpers shared by the AQLM kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aqlm {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Scheme ids used as template parameters.
+enum Scheme : int { kScheme2x8 = 0, kScheme1x16 = 1 };
+
+constexpr int kGroup = 8;          // g: inputs per group
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kCodewords2x8 = 256; // 2^B for B = 8
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(f16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+// 16x16x32 fp16 matrix-core product with fp32 accumulation:
+//   D[i][j] = C[i][j] + sum_k A[i][k] * B[k][j],
+// lane l supplies A[l % 16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l % 16] and
+// holds D[4*(l/16) + r][l % 16] for r = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Streaming (non-temporal) 16-byte load: codes are read exactly once.
+__device__ __forceinline__ u32x4 load_nt16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+}  // namespace aqlm

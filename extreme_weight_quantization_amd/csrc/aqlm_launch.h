@@ -1,0 +1,22 @@
+// Host-side launchers of the AQLM kernels (called by the C ABI in aqlm_api.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aqlm {
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_decode(int scheme, const void* codes, const void* codebooks, const void* scales,
+                         void* w, int64_t out, int64_t in, hipStream_t stream);
+
+hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, const void* scales,
+                       const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                       hipStream_t stream);
+
+hipError_t launch_gemm(int scheme, const void* codes, const void* codebooks, const void* scales,
+                       const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                       hipStream_t stream);
+
+}  // namespace aqlm

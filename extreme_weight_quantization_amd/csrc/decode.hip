@@ -1,0 +1,75 @@
+// Standalone dequantization: W16[out][in] from codes, codebooks and scales.
+//
+// "The AQLM Quantization Algorithm, Explained", section "What is
+// Multi-Codebook Quantization (MCQ)?", Figure 2: the codeword selected in
+// each codebook is looked up, the M codewords are summed, and the sum is
+// scaled by the output channel's factor.  This kernel fixes the arithmetic so
+// that the result is bit-exact: fp32 sum (codebook 0 first), fp32 product
+// with the scale, one fp16 rounding to nearest-even.
+//
+// One thread produces one group (8 fp16 = one 16-byte store).  The 2x8
+// codebooks (8 KB) are staged in LDS; 1x16 codewords are gathered from the
+// 1 MiB codebook through L2.  The kernel is bound by the W16 write stream.
+#include "aqlm_device.h"
+#include "aqlm_launch.h"
+
+namespace aqlm {
+
+#pragma clang fp contract(off)
+
+template <int SCHEME>
+__global__ __launch_bounds__(256) void decode_kernel(const uint8_t* __restrict__ codes,
+                                                     const f16* __restrict__ codebooks,
+                                                     const f16* __restrict__ scales,
+                                                     f16* __restrict__ w,
+                                                     uint32_t n_groups, uint32_t G) {
+    __shared__ u32x4 cb_lds[SCHEME == kScheme2x8 ? 2 * kCodewords2x8 : 1];
+    if constexpr (SCHEME == kScheme2x8) {
+        for (int i = threadIdx.x; i < 2 * kCodewords2x8; i += blockDim.x)
+            cb_lds[i] = load16(codebooks + (size_t)i * kGroup);
+        __syncthreads();
+    }
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x; gid < n_groups; gid += stride) {
+        const uint32_t row = gid / G;
+        const float s = (float)scales[row];
+        const uint32_t code = reinterpret_cast<const uint16_t*>(codes)[gid];
+        float v[kGroup];
+        if constexpr (SCHEME == kScheme2x8) {
+            // byte 0 indexes codebook 0, byte 1 codebook 1 ([out][G][M] layout)
+            const f16x8 c0 = as_f16x8(cb_lds[code & 0xff]);
+            const f16x8 c1 = as_f16x8(cb_lds[kCodewords2x8 + (code >> 8)]);
+#pragma unroll
+            for (int t = 0; t < kGroup; ++t) v[t] = __fadd_rn((float)c0[t], (float)c1[t]);
+        } else {
+            const f16x8 c0 = as_f16x8(load16(codebooks + (size_t)code * kGroup));
+#pragma unroll
+            for (int t = 0; t < kGroup; ++t) v[t] = (float)c0[t];
+        }
+        f16x8 o;
+#pragma unroll
+        for (int t = 0; t < kGroup; ++t) o[t] = (f16)__fmul_rn(v[t], s);
+        *reinterpret_cast<u32x4*>(w + (size_t)gid * kGroup) = as_u32x4(o);
+    }
+}
+
+hipError_t launch_decode(int scheme, const void* codes, const void* codebooks, const void* scales,
+                         void* w, int64_t out, int64_t in, hipStream_t stream) {
+    const uint32_t G = (uint32_t)(in / kGroup);
+    const uint64_t n_groups = (uint64_t)out * G;
+    const int block = 256;
+    uint64_t blocks = (n_groups + block - 1) / block;
+    const uint64_t max_blocks = (uint64_t)device_cu_count() * 16;
+    if (blocks > max_blocks) blocks = max_blocks;
+    if (scheme == kScheme2x8)
+        hipLaunchKernelGGL(decode_kernel<kScheme2x8>, dim3((unsigned)blocks), dim3(block), 0, stream,
+                           (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales, (f16*)w,
+                           (uint32_t)n_groups, G);
+    else
+        hipLaunchKernelGGL(decode_kernel<kScheme1x16>, dim3((unsigned)blocks), dim3(block), 0, stream,
+                           (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales, (f16*)w,
+                           (uint32_t)n_groups, G);
+    return hipGetLastError();
+}
+
+}  // namespace aqlm

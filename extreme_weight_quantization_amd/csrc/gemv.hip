@@ -1,0 +1,233 @@
+// Decode-phase product y[b][i] = s[i] * sum_k Wc[i][k] x[b][k], batch 1..16.
+//
+// "The AQLM Quantization Algorithm, Explained": weights are dequantized at
+// run time after being fetched from memory (section "Why and what do we
+// quantize?"); Figure 2 of the MCQ section gives the dequantization (sum of
+// one codeword per codebook, then the row scale).  Decoding is memory-bound
+// (same section), so this kernel streams every code byte exactly once and
+// keeps everything else on chip.
+//
+// Work decomposition (one workgroup of 16 waves per CU):
+//  * rows are cut into tiles of 16 (the M side of a 16x16x32 fp16 matrix-core
+//    product); a workgroup owns row tiles blockIdx.x, +gridDim.x, ...
+//  * the input dimension is cut into slabs of 32 groups (256 inputs); the
+//    waves of a workgroup take slabs round-robin, and for each slab keep the
+//    activation operand (x, batch padded to 16 columns) in registers while
+//    they run through the workgroup's row tiles;
+//  * lane l of a wave decodes group (slab, 8*(l/16) + q) of row l%16 for the
+//    q-th product, so one 16-byte code load per lane covers 8 products;
+//  * the 2x8 codebooks live in LDS, replicated REPL times with entry k of
+//    replica r at 16-byte slot (2k + m) * REPL + r; lane l reads replica
+//    l % REPL, which spreads the 16 lanes served together over distinct bank
+//    groups; 1x16 codewords are gathered from the L2-resident 1 MiB codebook;
+//  * per-wave partial tiles are summed in LDS; the row scale is applied once
+//    in fp32 and y is rounded to fp16.
+#include "aqlm_device.h"
+#include "aqlm_launch.h"
+
+namespace aqlm {
+
+constexpr int kGemvWaves = 16;
+constexpr int kGemvThreads = kGemvWaves * kWave;
+constexpr int kSlabGroups = 32;          // groups per slab (8 products x 4 k-quarters)
+constexpr int kRowTile = 16;
+constexpr int kRedFloats = kRowTile * 16; // one 16x16 fp32 tile per wave
+
+// Loads the 8 two-byte codes of lane's chunk (row, groups g0 .. g0+7).
+template <bool VEC>
+__device__ __forceinline__ u32x4 load_codes(const uint8_t* __restrict__ codes, int row, int out,
+                                            int g0, int G) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row >= out) return v;
+    const uint8_t* crow = codes + (size_t)row * G * 2;
+    if (VEC && g0 + 8 <= G) return load_nt16(crow + (size_t)g0 * 2);
+    const uint16_t* c16 = reinterpret_cast<const uint16_t*>(crow);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint32_t c = (g0 + q < G) ? (uint32_t)c16[g0 + q] : 0u;
+        v[q >> 1] |= c << (16 * (q & 1));
+    }
+    return v;
+}
+
+// Decodes the 8 groups of a code chunk into matrix-core A operands (fp16) and
+// accumulates their products with the activation operands bx into acc.
+// Groups past the end of the row (ok mask bit clear) contribute zero.  The
+// lookups of four groups are issued before any of them is consumed.
+template <int SCHEME, int REPL>
+__device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restrict__ cb_lds,
+                                            const f16* __restrict__ codebooks, int rrep,
+                                            uint32_t ok_mask, const f16x8 (&bx)[8], f32x4 acc) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        f16x8 a[4];
+        if constexpr (SCHEME == kScheme2x8) {
+            f16x8 c1[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t c = (cv[2 * h + (q >> 1)] >> (16 * (q & 1))) & 0xffff;
+                a[q] = as_f16x8(cb_lds[(2 * (c & 0xff)) * REPL + rrep]);
+                c1[q] = as_f16x8(cb_lds[(2 * (c >> 8) + 1) * REPL + rrep]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[q] = ((ok_mask >> (4 * h + q)) & 1) ? a[q] + c1[q] : f16x8{};
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t c = (cv[2 * h + (q >> 1)] >> (16 * (q & 1))) & 0xffff;
+                a[q] = as_f16x8(load16(codebooks + (size_t)c * kGroup));
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[q] = ((ok_mask >> (4 * h + q)) & 1) ? a[q] : f16x8{};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = mfma16x16x32(a[q], bx[4 * h + q], acc);
+    }
+    return acc;
+}
+
+template <int SCHEME, int REPL, bool VEC, int RTP>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __restrict__ codes,
+                                                            const f16* __restrict__ codebooks,
+                                                            const f16* __restrict__ scales,
+                                                            const f16* __restrict__ x,
+                                                            f16* __restrict__ y,
+                                                            int out, int in, int T) {
+    extern __shared__ u32x4 smem[];
+    constexpr int kCbSlots = (SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0;
+    float* red = reinterpret_cast<float*>(smem + kCbSlots);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int G = in / kGroup;
+    const int n_slab = (G + kSlabGroups - 1) / kSlabGroups;
+    const int n_rt = (out + kRowTile - 1) / kRowTile;
+
+    const int lrow = lane & 15;   // A row / B column (batch) of this lane
+    const int kq = lane >> 4;     // which 8-group quarter of the slab
+    const int rrep = lane % REPL; // codebook replica read by this lane
+
+    // First codes of this wave, issued before the codebook is staged so that
+    // the HBM latency overlaps the LDS fill.
+    int rt0 = blockIdx.x;
+    int s0 = wave;
+    u32x4 cnext[RTP];
+#pragma unroll
+    for (int i = 0; i < RTP; ++i) {
+        const int rt = rt0 + i * (int)gridDim.x;
+        cnext[i] = (s0 < n_slab && rt < n_rt)
+                       ? load_codes<VEC>(codes, rt * kRowTile + lrow, out, s0 * kSlabGroups + kq * 8, G)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    if constexpr (SCHEME == kScheme2x8) {
+        // Slot j holds entry (m, k) of replica r, j = (2k + m) * REPL + r; consecutive
+        // threads write consecutive slots (conflict-free), reading the same 16 B source.
+        for (int j = tid; j < kCbSlots; j += kGemvThreads) {
+            const int km = j / REPL;
+            const int m = km & 1, k = km >> 1;
+            smem[j] = load16(codebooks + (size_t)(m * kCodewords2x8 + k) * kGroup);
+        }
+    }
+    __syncthreads();
+
+    for (; rt0 < n_rt; rt0 += gridDim.x * RTP) {
+        f32x4 acc[RTP];
+#pragma unroll
+        for (int i = 0; i < RTP; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int s = s0; s < n_slab; s += kGemvWaves) {
+            const int g0 = s * kSlabGroups + kq * 8;   // first group of this lane's chunk
+            u32x4 ccur[RTP];
+#pragma unroll
+            for (int i = 0; i < RTP; ++i) ccur[i] = cnext[i];
+            // Prefetch the codes of this wave's next slab (or of the next pass).
+            {
+                int sn = s + kGemvWaves, rtn = rt0;
+                if (sn >= n_slab) { sn = wave; rtn = rt0 + (int)gridDim.x * RTP; }
+#pragma unroll
+                for (int i = 0; i < RTP; ++i) {
+                    const int rt = rtn + i * (int)gridDim.x;
+                    cnext[i] = (sn < n_slab && rt < n_rt)
+                                   ? load_codes<VEC>(codes, rt * kRowTile + lrow, out, sn * kSlabGroups + kq * 8, G)
+                                   : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            f16x8 bx[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int grp = g0 + q;
+                bx[q] = (lrow < T && grp < G)
+                            ? as_f16x8(load16(x + (size_t)lrow * in + (size_t)grp * kGroup))
+                            : f16x8{};
+            }
+            const uint32_t gmask = (G - g0 >= 8) ? 0xffu : (G > g0 ? (1u << (G - g0)) - 1u : 0u);
+#pragma unroll
+            for (int i = 0; i < RTP; ++i) {
+                const int rt = rt0 + i * (int)gridDim.x;
+                if (rt >= n_rt) break;
+                const uint32_t ok = (rt * kRowTile + lrow < out) ? gmask : 0u;
+                acc[i] = chunk_mfma<SCHEME, REPL>(ccur[i], smem, codebooks, rrep, ok, bx, acc[i]);
+            }
+        }
+
+        // Sum the per-wave partial tiles, scale, round to fp16.
+#pragma unroll
+        for (int i = 0; i < RTP; ++i) {
+            const int rt = rt0 + i * (int)gridDim.x;
+            if (rt >= n_rt) break;
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave * kRedFloats + (4 * kq + r) * 16 + lrow] = acc[i][r];
+            __syncthreads();
+            if (tid < kRedFloats) {
+                const int b = tid / kRowTile, rr = tid % kRowTile;
+                const int row = rt * kRowTile + rr;
+                if (b < T && row < out) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < kGemvWaves; ++w) sum += red[w * kRedFloats + rr * 16 + b];
+                    y[(size_t)b * out + row] = (f16)(sum * (float)scales[row]);
+                }
+            }
+        }
+    }
+}
+
+template <int SCHEME, int REPL, bool VEC, int RTP>
+static hipError_t launch_gemv_t(const void* codes, const void* codebooks, const void* scales,
+                                const void* x, void* y, int out, int in, int T, int grid,
+                                hipStream_t stream) {
+    auto kern = gemv_kernel<SCHEME, REPL, VEC, RTP>;
+    const size_t lds = (size_t)((SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0) * 16 +
+                       (size_t)kGemvWaves * kRedFloats * sizeof(float);
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemvThreads), lds, stream,
+                       (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales,
+                       (const f16*)x, (f16*)y, out, in, T);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, const void* scales,
+                       const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                       hipStream_t stream) {
+    constexpr int RTP = 2;
+    const int n_rt = (int)((out + kRowTile - 1) / kRowTile);
+    const int cus = device_cu_count();
+    const int grid = n_rt < cus ? n_rt : cus;
+    const bool vec = (in % 64) == 0;   // 16-byte aligned code rows
+    const int o = (int)out, n = (int)in, T = (int)batch;
+    if (scheme == kScheme2x8) {
+        return vec ? launch_gemv_t<kScheme2x8, 16, true, RTP>(codes, codebooks, scales, x, y, o, n, T, grid, stream)
+                   : launch_gemv_t<kScheme2x8, 16, false, RTP>(codes, codebooks, scales, x, y, o, n, T, grid, stream);
+    }
+    return vec ? launch_gemv_t<kScheme1x16, 1, true, RTP>(codes, codebooks, scales, x, y, o, n, T, grid, stream)
+               : launch_gemv_t<kScheme1x16, 1, false, RTP>(codes, codebooks, scales, x, y, o, n, T, grid, stream);
+}
+
+}  // namespace aqlm

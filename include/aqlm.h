@@ -1,0 +1,106 @@
+/*
+ * aqlm.h - C ABI of libaqlm.so: the AQLM 2-bit quantized linear layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Representation ("The AQLM Quantization Algorithm, Explained", section
+ * "What is Multi-Codebook Quantization (MCQ)?" and Figure 2): a weight matrix
+ * W of shape [out][in] (W.X convention, rows are output channels) is cut
+ * row-wise into groups of g consecutive inputs.  Group j of row i is the sum
+ * of M codewords, one from each of M codebooks of 2^B fp16 codewords of
+ * length g, then multiplied by the row's fp16 scale:
+ *
+ *     W[i][j*g + t] = s[i] * sum_{m=0}^{M-1} C_m[ code[i][j][m] ][t]
+ *
+ * Supported schemes (named XBit-MxB on the same page, section "Key AQLM
+ * quantization parameters"): (M, B, g) = (1, 16, 8) "1x16" and (2, 8, 8)
+ * "2x8", both 2 bits per weight in the codes.
+ *
+ * Memory layouts (all arrays contiguous, row-major, DEVICE pointers):
+ *   codes      [out][in/g][M]  uint8 for B = 8; int16 for B = 16, where the
+ *                              16-bit pattern read as unsigned is the index
+ *   codebooks  [M][2^B][g]     fp16 (IEEE binary16, passed as opaque 16-bit
+ *                              storage)
+ *   scales     [out]           fp16
+ *   x          [batch][in]     fp16 activations
+ *   y          [batch][out]    fp16 outputs (decode: W16 [out][in])
+ *
+ * Ownership: the caller owns every buffer.  No entry point keeps a pointer
+ * after it returns, and none allocates device memory.
+ *
+ * Asynchrony: every call validates its arguments on the host, enqueues its
+ * kernels on `stream` (a hipStream_t; NULL means the null stream) and
+ * returns.  Execution errors surface at the caller's next synchronisation.
+ * Calls are reentrant and thread-safe.  A call with out == 0 (or, for GEMV
+ * and GEMM, batch == 0) enqueues nothing and returns AQLM_OK once the scheme
+ * and shape are valid; its pointers may then be NULL.
+ *
+ * Numerics: GEMV and GEMM accumulate in fp32 and round y to fp16 once
+ * (nearest-even).  Decode is bit-exact: per weight, the fp32 sum of the M
+ * codewords (codebook 0 first, then m ascending, the sum starting from
+ * codebook 0's codeword), times the fp32 scale, rounded to fp16 nearest-even
+ * with subnormals kept.
+ */
+#ifndef AQLM_H
+#define AQLM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    AQLM_OK = 0,
+    AQLM_ERR_NULL = 1,   /* a required pointer is NULL (or decode got x != NULL) */
+    AQLM_ERR_SHAPE = 2,  /* out/in/batch negative or out of range, in % g != 0 */
+    AQLM_ERR_SCHEME = 3, /* (M, B, g) not one of (1,16,8), (2,8,8) */
+    AQLM_ERR_ALIGN = 4,  /* codes, codebooks, x or y not 16-byte aligned, scales not 2-byte aligned */
+    AQLM_ERR_HIP = 5     /* the HIP runtime reported an error at launch */
+} aqlm_status;
+
+/* Largest `in` accepted (inputs per row). */
+#define AQLM_MAX_IN (1 << 20)
+/* Largest batch of aqlm_linear_gemv. */
+#define AQLM_GEMV_MAX_BATCH 16
+
+/*
+ * y[b][i] = sum_k W[i][k] * x[b][k] for b < batch, with W decoded on the fly
+ * (Figure 2 of the MCQ section: weights are dequantized after being fetched,
+ * then multiplied).  Decode-phase matrix-vector product: 1 <= batch <= 16.
+ * Requires 1 <= in <= AQLM_MAX_IN, in % g == 0, out <= 2^31 - 16.
+ */
+int aqlm_linear_gemv(const void* codes, const void* codebooks, const void* scales,
+                     const void* x, void* y, int M, int B, int g,
+                     int64_t out, int64_t in, int64_t batch, void* stream);
+
+/*
+ * Same product for a prefill batch of `batch` >= 1 tokens (batch <= 2^31 - 1):
+ * W tiles are decoded into LDS and fed to fp16 matrix cores with fp32
+ * accumulation.
+ */
+int aqlm_linear_gemm(const void* codes, const void* codebooks, const void* scales,
+                     const void* x, void* y, int M, int B, int g,
+                     int64_t out, int64_t in, int64_t batch, void* stream);
+
+/*
+ * Writes the dequantized fp16 weights W16[out][in] to y (bit-exact as stated
+ * above).  x must be NULL; batch is ignored.
+ */
+int aqlm_linear_decode(const void* codes, const void* codebooks, const void* scales,
+                       const void* x, void* y, int M, int B, int g,
+                       int64_t out, int64_t in, int64_t batch, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* aqlm_status_str(int status);
+
+/* hipError_t of the calling thread's last AQLM_ERR_HIP (0 if none). */
+int aqlm_last_hip_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* aqlm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AQLM_H */

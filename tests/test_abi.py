@@ -1,0 +1,117 @@
+"""C-ABI library checks that need no GPU: the library loads, exports every
+symbol that include/aqlm.h declares, and rejects bad arguments on the host
+before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import extreme_weight_quantization_amd as E
+from extreme_weight_quantization_amd import binding
+from extreme_weight_quantization_amd.build import LIB_PATH, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aqlm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        build()
+    return E.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aqlm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("aqlm_linear_gemv", "aqlm_linear_gemm", "aqlm_linear_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in aqlm.h but not exported"
+    assert set(declared_functions()) == set(binding.EXPORTED)
+
+
+def test_exports_are_plain_c_symbols():
+    out = os.popen(f"nm -D --defined-only {LIB_PATH}").read()
+    exported = set(re.findall(r" T (aqlm_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert binding.status_str(s).startswith("AQLM_")
+    assert "unknown" in binding.status_str(99)
+    assert lib.aqlm_version().decode().count(".") == 2
+    assert lib.aqlm_last_hip_error() == 0
+
+
+A = 1 << 20  # a 16-byte aligned fake device address: validation never dereferences it
+
+VALID = dict(codes=A, codebooks=A, scales=A, x=A, y=A, M=2, B=8, g=8, out=16, n_in=64, batch=1)
+
+
+def call(fn, **kw):
+    a = dict(VALID, **kw)
+    return binding.raw_call(fn, a["codes"], a["codebooks"], a["scales"], a["x"], a["y"], a["M"],
+                            a["B"], a["g"], a["out"], a["n_in"], a["batch"])
+
+
+@pytest.mark.parametrize("fn", ["aqlm_linear_gemv", "aqlm_linear_gemm"])
+def test_validation_product(lib, fn):
+    assert call(fn, codes=0) == binding.AQLM_ERR_NULL
+    assert call(fn, codebooks=0) == binding.AQLM_ERR_NULL
+    assert call(fn, scales=0) == binding.AQLM_ERR_NULL
+    assert call(fn, x=0) == binding.AQLM_ERR_NULL
+    assert call(fn, y=0) == binding.AQLM_ERR_NULL
+    for M, B, g in ((3, 8, 8), (2, 16, 8), (1, 8, 8), (2, 8, 16), (1, 16, 4)):
+        assert call(fn, M=M, B=B, g=g) == binding.AQLM_ERR_SCHEME
+    assert call(fn, n_in=60) == binding.AQLM_ERR_SHAPE
+    assert call(fn, n_in=0) == binding.AQLM_ERR_SHAPE
+    assert call(fn, n_in=(1 << 20) + 8) == binding.AQLM_ERR_SHAPE
+    assert call(fn, out=-1) == binding.AQLM_ERR_SHAPE
+    assert call(fn, batch=-1) == binding.AQLM_ERR_SHAPE
+    assert call(fn, out=1 << 31) == binding.AQLM_ERR_SHAPE
+    assert call(fn, codes=A + 8) == binding.AQLM_ERR_ALIGN
+    assert call(fn, x=A + 2) == binding.AQLM_ERR_ALIGN
+    assert call(fn, y=A + 4) == binding.AQLM_ERR_ALIGN
+    assert call(fn, codebooks=A + 8) == binding.AQLM_ERR_ALIGN
+    assert call(fn, scales=A + 1) == binding.AQLM_ERR_ALIGN
+    # empty problems enqueue nothing
+    assert call(fn, out=0) == binding.AQLM_OK
+    assert call(fn, batch=0) == binding.AQLM_OK
+
+
+def test_validation_gemv_batch_limit(lib):
+    assert call("aqlm_linear_gemv", batch=17) == binding.AQLM_ERR_SHAPE
+    assert call("aqlm_linear_gemm", batch=17, out=0) == binding.AQLM_OK
+
+
+def test_validation_decode(lib):
+    assert call("aqlm_linear_decode", x=A) == binding.AQLM_ERR_NULL   # decode takes no x
+    assert call("aqlm_linear_decode", x=0, y=0) == binding.AQLM_ERR_NULL
+    assert call("aqlm_linear_decode", x=0, M=1, B=8) == binding.AQLM_ERR_SCHEME
+    assert call("aqlm_linear_decode", x=0, n_in=12) == binding.AQLM_ERR_SHAPE
+    assert call("aqlm_linear_decode", x=0, out=1 << 30, n_in=1 << 10) == binding.AQLM_ERR_SHAPE
+    assert call("aqlm_linear_decode", x=0, y=A + 8) == binding.AQLM_ERR_ALIGN
+    assert call("aqlm_linear_decode", x=0, out=0) == binding.AQLM_OK
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    codes = torch.zeros((4, 8, 2), dtype=torch.uint8)
+    cb = torch.zeros((2, 256, 8), dtype=torch.float16)
+    s = torch.ones(4, dtype=torch.float16)
+    x = torch.zeros((1, 64), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        E.aqlm_linear_gemv(codes, cb, s, x)
+    with pytest.raises(ValueError):
+        E.aqlm_linear_decode(codes, cb, s)
