@@ -225,6 +225,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline only, no breakdown or CPU leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 64 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -314,6 +316,14 @@ def main():
             nbytes = 4096 * 4096 // 4 + 2 * 4096 + 2 * 4096 * 4096
             dc[f"{scheme}_4096x4096"] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
         breakdown["decode"] = dc
+
+    if args.copy_probe:
+        src = torch.empty(32 << 20, dtype=torch.float16, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None if (args.quick or args.no_cpu) else cpu_baseline()
 
