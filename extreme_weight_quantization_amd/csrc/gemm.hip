@@ -2,16 +2,20 @@
 //
 // "The AQLM Quantization Algorithm, Explained", Figure 2 of the MCQ section:
 // the matrix product runs on dequantized half-precision weights.  Each
-// workgroup owns a 256-token x 128-row output tile.  Per k-step of 64 inputs
-// it decodes the 128 x 64 W tile (1024 groups) into LDS as fp16, stages the
-// matching 256 x 64 X tile next to it, and runs 16x16x32 fp16 matrix-core
-// products with fp32 accumulation.  LDS is double-buffered: the global loads
-// and the codebook lookups of step k+1 are in flight while step k's
-// products run, so one barrier per step suffices.  The row scale is applied
-// once in the epilogue.
+// workgroup owns a BM-token x BN-row output tile.  Per k-step of 64 inputs it
+// decodes the BN x 64 W tile into LDS as fp16, stages the matching BM x 64
+// X tile next to it, and runs 16x16x32 fp16 matrix-core products with fp32
+// accumulation; the row scale is applied once in the epilogue.
 //
-// 2x8 codewords come from an LDS copy of the two codebooks (two interleaved
-// replicas); 1x16 codewords are gathered from the L2-resident codebook.
+// Software pipeline (one barrier per k-step, LDS double-buffered):
+//   top of step k : write the X chunks and decoded W groups of step k+1
+//                   (already in registers) into the idle LDS buffer, then
+//                   issue the global loads of step k+2;
+//   body          : fragment reads and products of step k;
+//   barrier.
+// 2x8 codewords come from an LDS copy of the two codebooks (interleaved
+// replicas); 1x16 codewords are gathered from the L2-resident codebook one
+// step earlier than they are written, from codes loaded one step before that.
 // Consecutive workgroups take consecutive token tiles of one W tile, so with
 // 8 token tiles every XCD keeps one X tile in its L2.
 #include "aqlm_device.h"
@@ -19,192 +23,231 @@
 
 namespace aqlm {
 
-constexpr int kBM = 256;             // tokens per workgroup tile
-constexpr int kBN = 128;             // output rows per workgroup tile
-constexpr int kBK = 64;              // inputs per k-step
-constexpr int kBKG = kBK / kGroup;   // groups per k-step (8)
-constexpr int kLdsStride = kBK + 8;  // fp16 per LDS row (+16 B: conflict-free 16 B reads)
-constexpr int kGemmThreads = 512;    // 8 waves: 4 along tokens x 2 along rows, 64 x 64 each
-constexpr int kGemmRepl = 2;
-constexpr int kXChunks = kBM * kBKG / kGemmThreads;   // 16-byte X chunks per thread (4)
-constexpr int kWGroups = kBN * kBKG / kGemmThreads;   // W groups decoded per thread (2)
-constexpr int kXTile = kBM * kLdsStride;              // fp16 elements
-constexpr int kWTile = kBN * kLdsStride;
-
-template <int SCHEME>
-struct GemmLds {
-    f16 xs[2][kXTile];
-    f16 ws[2][kWTile];
-    u32x4 cb[SCHEME == kScheme2x8 ? 2 * kCodewords2x8 * kGemmRepl : 1];
+template <int SCHEME, int BM, int BN, int WAVES_M, int WAVES_N, int REPL, int BK = 64, int MINB = 1>
+struct GemmCfg {
+    static constexpr int kBK = BK;                  // inputs per k-step
+    static constexpr int kBKG = BK / kGroup;        // groups per k-step
+    static constexpr int kLdsStride = BK + 8;       // fp16 per LDS row (+16 B: conflict-free 16 B reads)
+    static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+    static constexpr int kWM = BM / WAVES_M;        // wave tile (tokens)
+    static constexpr int kWN = BN / WAVES_N;        // wave tile (rows)
+    static constexpr int kFM = kWM / 16;            // 16x16 blocks per wave
+    static constexpr int kFN = kWN / 16;
+    static constexpr int kXChunks = BM * kBKG / kThreads;   // 16-byte X chunks per thread
+    static constexpr int kWGroups = BN * kBKG / kThreads;   // W groups per thread
+    static constexpr int kXTile = BM * kLdsStride;
+    static constexpr int kWTile = BN * kLdsStride;
+    static constexpr int kCbSlots = SCHEME == kScheme2x8 ? 2 * kCodewords2x8 * REPL : 1;
+    static constexpr size_t kLds = (size_t)2 * (kXTile + kWTile) * 2 + (size_t)kCbSlots * 16;
+    static_assert(BM * kBKG % kThreads == 0 && BN * kBKG % kThreads == 0, "tile/threads mismatch");
+    static_assert(kWGroups == 1 || kWGroups == 2 || kWGroups == 4 || kWGroups == 8, "W groups per thread");
+    static_assert(kLds * MINB <= 163840, "LDS budget");
 };
 
-// Codes of this thread's kWGroups groups (row r, groups gq0, gq0+1) at k-step ks.
-__device__ __forceinline__ uint32_t gemm_load_codes(const uint8_t* __restrict__ codes, int row,
-                                                    int out, int grp, int G) {
-    if (row >= out) return 0u;
-    const uint16_t* c16 = reinterpret_cast<const uint16_t*>(codes) + (size_t)row * G;
-    if ((G & 1) == 0 && grp + 1 < G) return *reinterpret_cast<const uint32_t*>(c16 + grp);
-    uint32_t v = 0;
-    if (grp < G) v = c16[grp];
-    if (grp + 1 < G) v |= (uint32_t)c16[grp + 1] << 16;
-    return v;
-}
-
-template <int SCHEME>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __restrict__ codes,
-                                                            const f16* __restrict__ codebooks,
-                                                            const f16* __restrict__ scales,
-                                                            const f16* __restrict__ x,
-                                                            f16* __restrict__ y,
-                                                            int out, int in, int T) {
-    __shared__ GemmLds<SCHEME> L;
+template <int SCHEME, int BM, int BN, int WAVES_M, int WAVES_N, int REPL, int BK, int MINB, bool PIPE>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void gemm_kernel(
+    const uint8_t* __restrict__ codes, const f16* __restrict__ codebooks,
+    const f16* __restrict__ scales, const f16* __restrict__ x, f16* __restrict__ y,
+    int out, int in, int T) {
+    using C = GemmCfg<SCHEME, BM, BN, WAVES_M, WAVES_N, REPL, BK, MINB>;
+    constexpr int kBKG = C::kBKG;
+    constexpr int kLdsStride = C::kLdsStride;
+    extern __shared__ u32x4 smem[];
+    f16* xs = reinterpret_cast<f16*>(smem);                 // [2][kXTile]
+    f16* ws = xs + 2 * C::kXTile;                            // [2][kWTile]
+    u32x4* cb = reinterpret_cast<u32x4*>(ws + 2 * C::kWTile);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int G = in / kGroup;
-    const int n_tt = (T + kBM - 1) / kBM;
-    const int n0 = (int)(blockIdx.x / n_tt) * kBN;   // first output row of the tile
-    const int t0 = (int)(blockIdx.x % n_tt) * kBM;   // first token of the tile
+    const int n_tt = (T + BM - 1) / BM;
+    const int n0 = (int)(blockIdx.x / n_tt) * BN;   // first output row of the tile
+    const int t0 = (int)(blockIdx.x % n_tt) * BM;   // first token of the tile
     const int n_k = (G + kBKG - 1) / kBKG;
 
-    // W decode role: row wr of the tile, groups wg0, wg0+1 of each k-step.
-    const int wr = tid >> 2;
-    const int wg0 = (tid & 3) * kWGroups;
+    // W decode role: row wr of the tile, groups wg0 .. wg0 + kWGroups - 1 of each step.
+    constexpr int kThrPerRow = kBKG / C::kWGroups;
+    const int wr = tid / kThrPerRow;
+    const int wg0 = (tid % kThrPerRow) * C::kWGroups;
     const int wrow = n0 + wr;
-    const int rep = tid % kGemmRepl;
+    const bool wrow_ok = wrow < out;
+    const int rep = tid % REPL;
 
     if constexpr (SCHEME == kScheme2x8) {
-        for (int j = tid; j < 2 * kCodewords2x8 * kGemmRepl; j += kGemmThreads) {
-            const int km = j / kGemmRepl;
-            L.cb[j] = load16(codebooks + (size_t)((km & 1) * kCodewords2x8 + (km >> 1)) * kGroup);
+        for (int j = tid; j < C::kCbSlots; j += C::kThreads) {
+            const int km = j / REPL;
+            cb[j] = load16(codebooks + (size_t)((km & 1) * kCodewords2x8 + (km >> 1)) * kGroup);
         }
     }
 
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    auto load_x = [&](int ks, u32x4 (&xr)[kXChunks]) {
+    // ---- stage helpers --------------------------------------------------
+    auto load_x = [&](int ks, u32x4 (&xr)[C::kXChunks]) {
 #pragma unroll
-        for (int it = 0; it < kXChunks; ++it) {
-            const int c = it * kGemmThreads + tid;
+        for (int it = 0; it < C::kXChunks; ++it) {
+            const int c = it * C::kThreads + tid;
             const int r = c / kBKG, gq = c % kBKG;
             const int tok = t0 + r, grp = ks * kBKG + gq;
             xr[it] = (tok < T && grp < G) ? load16(x + (size_t)tok * in + (size_t)grp * kGroup) : zero4;
         }
     };
-    auto store_x = [&](int buf, const u32x4 (&xr)[kXChunks]) {
+    auto store_x = [&](int buf, const u32x4 (&xr)[C::kXChunks]) {
+        f16* dst = xs + buf * C::kXTile;
 #pragma unroll
-        for (int it = 0; it < kXChunks; ++it) {
-            const int c = it * kGemmThreads + tid;
+        for (int it = 0; it < C::kXChunks; ++it) {
+            const int c = it * C::kThreads + tid;
             const int r = c / kBKG, gq = c % kBKG;
-            *reinterpret_cast<u32x4*>(&L.xs[buf][r * kLdsStride + gq * kGroup]) = xr[it];
+            *reinterpret_cast<u32x4*>(dst + r * kLdsStride + gq * kGroup) = xr[it];
         }
     };
-    // Decodes this thread's two groups of k-step ks (codes cv) into wr[].
-    auto decode_w = [&](int ks, uint32_t cv, u32x4 (&wv)[kWGroups]) {
+    // Codes of this thread's groups at step ks, one 16-bit code per entry.  The
+    // loads are unconditional (indices clamped into the matrix) so that no
+    // branch forces a wait on them; groups outside the matrix are masked when
+    // they are decoded.
+    const uint16_t* crow_c = reinterpret_cast<const uint16_t*>(codes) + (size_t)(wrow_ok ? wrow : out - 1) * G;
+    auto load_codes = [&](int ks, uint32_t (&cv)[C::kWGroups]) {
+        const int grp = ks * kBKG + wg0;
 #pragma unroll
-        for (int q = 0; q < kWGroups; ++q) {
-            const uint32_t c = (cv >> (16 * q)) & 0xffff;
-            const bool ok = (wrow < out) && (ks * kBKG + wg0 + q < G);
-            if constexpr (SCHEME == kScheme2x8) {
-                const f16x8 c0 = as_f16x8(L.cb[(2 * (c & 0xff)) * kGemmRepl + rep]);
-                const f16x8 c1 = as_f16x8(L.cb[(2 * (c >> 8) + 1) * kGemmRepl + rep]);
-                wv[q] = ok ? as_u32x4(c0 + c1) : zero4;
-            } else {
-                const u32x4 v = load16(codebooks + (size_t)c * kGroup);
-                wv[q] = ok ? v : zero4;
-            }
+        for (int q = 0; q < C::kWGroups; ++q) cv[q] = crow_c[min(grp + q, G - 1)];
+    };
+    auto group_ok = [&](int ks, int q) { return wrow_ok && (ks * kBKG + wg0 + q < G); };
+    // 1x16: gather the codewords (zero for groups outside the matrix).
+    auto gather_w = [&](int ks, const uint32_t (&cv)[C::kWGroups], u32x4 (&wv)[C::kWGroups]) {
+#pragma unroll
+        for (int q = 0; q < C::kWGroups; ++q) {
+            const u32x4 v = load16(codebooks + (size_t)cv[q] * kGroup);
+            wv[q] = group_ok(ks, q) ? v : zero4;
         }
     };
-    auto store_w = [&](int buf, const u32x4 (&wv)[kWGroups]) {
+    // 2x8: sum the two codewords from the LDS codebook copy.
+    auto lookup_w = [&](int ks, const uint32_t (&cv)[C::kWGroups], u32x4 (&wv)[C::kWGroups]) {
 #pragma unroll
-        for (int q = 0; q < kWGroups; ++q)
-            *reinterpret_cast<u32x4*>(&L.ws[buf][wr * kLdsStride + (wg0 + q) * kGroup]) = wv[q];
+        for (int q = 0; q < C::kWGroups; ++q) {
+            const f16x8 c0 = as_f16x8(cb[(2 * (cv[q] & 0xff)) * REPL + rep]);
+            const f16x8 c1 = as_f16x8(cb[(2 * (cv[q] >> 8) + 1) * REPL + rep]);
+            wv[q] = group_ok(ks, q) ? as_u32x4(c0 + c1) : zero4;
+        }
+    };
+    auto store_w = [&](int buf, const u32x4 (&wv)[C::kWGroups]) {
+        f16* dst = ws + buf * C::kWTile + wr * kLdsStride + wg0 * kGroup;
+#pragma unroll
+        for (int q = 0; q < C::kWGroups; ++q) *reinterpret_cast<u32x4*>(dst + q * kGroup) = wv[q];
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[C::kFM][C::kFN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < C::kFN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: step 0 into buffer 0; codes of step 1 in flight.
-    u32x4 xr[kXChunks];
-    u32x4 wv[kWGroups];
-    uint32_t c_next = gemm_load_codes(codes, wrow, out, 0 * kBKG + wg0, G);
+    // All fragments of the step are read before the first product, and the
+    // scheduler is not allowed to sink the reads next to their uses, so the
+    // products never wait on LDS latency one pair at a time.
+    auto mma_step = [&](int buf) {
+        const f16* xsb = xs + buf * C::kXTile + (wm * C::kWM + (lane & 15)) * kLdsStride;
+        const f16* wsb = ws + buf * C::kWTile + (wn * C::kWN + (lane & 15)) * kLdsStride;
+        constexpr int KK = BK / 32;
+        f16x8 a[KK][C::kFM], b[KK][C::kFN];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int kc = kk * 32 + 8 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i) a[kk][i] = *reinterpret_cast<const f16x8*>(xsb + i * 16 * kLdsStride + kc);
+#pragma unroll
+            for (int j = 0; j < C::kFN; ++j) b[kk][j] = *reinterpret_cast<const f16x8*>(wsb + j * 16 * kLdsStride + kc);
+        }
+        if constexpr (PIPE) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kFN; ++j) acc[i][j] = mfma16x16x32(a[kk][i], b[kk][j], acc[i][j]);
+    };
+
+    // ---- prologue ---------------------------------------------------------
+    u32x4 xr[C::kXChunks];
+    u32x4 wv[C::kWGroups];
+    uint32_t c1[C::kWGroups], c2[C::kWGroups];   // codes of steps k+1 and k+2 (1x16: k+2, k+3)
+    load_codes(0, c1);
     load_x(0, xr);
-    uint32_t c_cur = c_next;
-    c_next = (n_k > 1) ? gemm_load_codes(codes, wrow, out, 1 * kBKG + wg0, G) : 0u;
-    __syncthreads();   // codebook staged
-    decode_w(0, c_cur, wv);
+    __syncthreads();   // codebook copy staged
+    if constexpr (SCHEME == kScheme2x8) lookup_w(0, c1, wv); else gather_w(0, c1, wv);
     store_x(0, xr);
     store_w(0, wv);
+    // step 1 in registers
+    load_codes(1, c1);
+    load_x(1, xr);
+    if constexpr (SCHEME == kScheme1x16) {
+        gather_w(1, c1, wv);
+        load_codes(2, c2);
+    }
     __syncthreads();
 
-    for (int ks = 0; ks < n_k; ++ks) {
-        const int buf = ks & 1;
-        const bool more = ks + 1 < n_k;
-        if (more) {
-            load_x(ks + 1, xr);
-            c_cur = c_next;
-            c_next = (ks + 2 < n_k) ? gemm_load_codes(codes, wrow, out, (ks + 2) * kBKG + wg0, G) : 0u;
-            if constexpr (SCHEME == kScheme1x16) decode_w(ks + 1, c_cur, wv);   // gathers in flight
+    // ---- main loop: steps 0 .. n_k-2 --------------------------------------
+    for (int ks = 0; ks + 1 < n_k; ++ks) {
+        const int nb = (ks + 1) & 1;
+        if constexpr (SCHEME == kScheme2x8) {
+            lookup_w(ks + 1, c1, wv);
+            store_x(nb, xr);
+            store_w(nb, wv);
+            load_codes(ks + 2, c1);
+            load_x(ks + 2, xr);
+        } else {
+            store_x(nb, xr);
+            store_w(nb, wv);
+            gather_w(ks + 2, c2, wv);
+            load_codes(ks + 3, c2);
+            load_x(ks + 2, xr);
         }
-        const f16* xsb = L.xs[buf];
-        const f16* wsb = L.ws[buf];
-#pragma unroll
-        for (int kk = 0; kk < kBK / 32; ++kk) {
-            const int kc = kk * 32 + 8 * (lane >> 4);
-            f16x8 a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const f16x8*>(xsb + (wm * 64 + i * 16 + (lane & 15)) * kLdsStride + kc);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const f16x8*>(wsb + (wn * 64 + j * 16 + (lane & 15)) * kLdsStride + kc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
-        }
-        if (more) {
-            if constexpr (SCHEME == kScheme2x8) decode_w(ks + 1, c_cur, wv);
-            store_x(buf ^ 1, xr);
-            store_w(buf ^ 1, wv);
-        }
+        mma_step(ks & 1);
         __syncthreads();
     }
+    mma_step((n_k - 1) & 1);
 
-    // Epilogue: lane holds D[4*(l/16)+r][l%16] of block (i, j): token rows, output columns.
+    // ---- epilogue: lane holds D[4*(l/16)+r][l%16] of block (i, j) ------------
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
+    for (int j = 0; j < C::kFN; ++j) {
+        const int col = n0 + wn * C::kWN + j * 16 + (lane & 15);
         if (col >= out) continue;
         const float s = (float)scales[col];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < C::kFM; ++i) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int tok = t0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+                const int tok = t0 + wm * C::kWM + i * 16 + 4 * (lane >> 4) + r;
                 if (tok < T) y[(size_t)tok * out + col] = (f16)(acc[i][j][r] * s);
             }
         }
     }
 }
 
+template <int SCHEME, int BM, int BN, int WAVES_M, int WAVES_N, int REPL, int BK = 64, int MINB = 1, bool PIPE = true>
+hipError_t launch_gemm_t(const void* codes, const void* codebooks, const void* scales,
+                         const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                         hipStream_t stream) {
+    using C = GemmCfg<SCHEME, BM, BN, WAVES_M, WAVES_N, REPL, BK, MINB>;
+    auto kern = gemm_kernel<SCHEME, BM, BN, WAVES_M, WAVES_N, REPL, BK, MINB, PIPE>;
+    if (C::kLds > 65536) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLds);
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)(((out + BN - 1) / BN) * ((batch + BM - 1) / BM)));
+    hipLaunchKernelGGL(kern, grid, dim3(C::kThreads), C::kLds, stream, (const uint8_t*)codes,
+                       (const f16*)codebooks, (const f16*)scales, (const f16*)x, (f16*)y,
+                       (int)out, (int)in, (int)batch);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(int scheme, const void* codes, const void* codebooks, const void* scales,
                        const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                        hipStream_t stream) {
-    const dim3 grid((unsigned)(((out + kBN - 1) / kBN) * ((batch + kBM - 1) / kBM)));
     if (scheme == kScheme2x8)
-        hipLaunchKernelGGL(gemm_kernel<kScheme2x8>, grid, dim3(kGemmThreads), 0, stream,
-                           (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales,
-                           (const f16*)x, (f16*)y, (int)out, (int)in, (int)batch);
-    else
-        hipLaunchKernelGGL(gemm_kernel<kScheme1x16>, grid, dim3(kGemmThreads), 0, stream,
-                           (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales,
-                           (const f16*)x, (f16*)y, (int)out, (int)in, (int)batch);
-    return hipGetLastError();
+        return launch_gemm_t<kScheme2x8, 256, 128, 4, 2, 2>(codes, codebooks, scales, x, y, out, in, batch, stream);
+    return launch_gemm_t<kScheme1x16, 256, 128, 4, 2, 1>(codes, codebooks, scales, x, y, out, in, batch, stream);
 }
 
 }  // namespace aqlm

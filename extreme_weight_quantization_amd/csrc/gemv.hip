@@ -33,21 +33,25 @@ constexpr int kSlabGroups = 32;          // groups per slab (8 products x 4 k-qu
 constexpr int kRowTile = 16;
 constexpr int kRedFloats = kRowTile * 16; // one 16x16 fp32 tile per wave
 
-// Loads the 8 two-byte codes of lane's chunk (row, groups g0 .. g0+7).
+// Loads the 8 two-byte codes of a lane's chunk (row, groups g0 .. g0+7),
+// packed two per 32-bit word.  The load is unconditional, with the row and
+// group indices clamped into the matrix, so that no branch forces an early
+// wait on it; groups outside the matrix are masked when they are decoded.
 template <bool VEC>
 __device__ __forceinline__ u32x4 load_codes(const uint8_t* __restrict__ codes, int row, int out,
                                             int g0, int G) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row >= out) return v;
-    const uint8_t* crow = codes + (size_t)row * G * 2;
-    if (VEC && g0 + 8 <= G) return load_nt16(crow + (size_t)g0 * 2);
-    const uint16_t* c16 = reinterpret_cast<const uint16_t*>(crow);
+    const int r = min(row, out - 1);
+    const uint16_t* c16 = reinterpret_cast<const uint16_t*>(codes) + (size_t)r * G;
+    if constexpr (VEC) {
+        // G % 8 == 0: 16-byte aligned chunks; a chunk past the end is clamped to the last one.
+        return load_nt16(c16 + min(g0, G - 8));
+    } else {
+        u32x4 v;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const uint32_t c = (g0 + q < G) ? (uint32_t)c16[g0 + q] : 0u;
-        v[q >> 1] |= c << (16 * (q & 1));
+        for (int q = 0; q < 4; ++q)
+            v[q] = (uint32_t)c16[min(g0 + 2 * q, G - 1)] | ((uint32_t)c16[min(g0 + 2 * q + 1, G - 1)] << 16);
+        return v;
     }
-    return v;
 }
 
 // Decodes the 8 groups of a code chunk into matrix-core A operands (fp16) and
@@ -108,8 +112,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
     const int kq = lane >> 4;     // which 8-group quarter of the slab
     const int rrep = lane % REPL; // codebook replica read by this lane
 
-    // First codes of this wave, issued before the codebook is staged so that
-    // the HBM latency overlaps the LDS fill.
+    // First codes and activations of this wave, issued before the codebook is
+    // staged so that their memory latency overlaps the LDS fill.
     int rt0 = blockIdx.x;
     int s0 = wave;
     u32x4 cnext[RTP];
@@ -120,14 +124,46 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
                        ? load_codes<VEC>(codes, rt * kRowTile + lrow, out, s0 * kSlabGroups + kq * 8, G)
                        : u32x4{0u, 0u, 0u, 0u};
     }
+    f16x8 bx[8];
+    auto load_x = [&](int s) {
+        const int g0 = s * kSlabGroups + kq * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int grp = g0 + q;
+            bx[q] = (lrow < T && grp < G)
+                        ? as_f16x8(load16(x + (size_t)lrow * in + (size_t)grp * kGroup))
+                        : f16x8{};
+        }
+    };
+    load_x(s0);
+    int s_loaded = s0;   // slab whose activations are in bx
+
+    // 1x16: warm this XCD's L2 with a 32 KB slice of the codebook (workgroups
+    // are dealt to the 8 XCDs round-robin, so 32 consecutive workgroups of one
+    // XCD cover the whole 1 MiB); the gathers that follow then hit in L2.
+    u32x4 warm = {0u, 0u, 0u, 0u};
+    if constexpr (SCHEME == kScheme1x16) {
+        const size_t slice = (size_t)((blockIdx.x >> 3) & 31) * (32768 / 16);
+        const u32x4* cb16 = reinterpret_cast<const u32x4*>(codebooks);
+        warm = load16(cb16 + slice + tid) ^ load16(cb16 + slice + kGemvThreads + tid);
+    }
 
     if constexpr (SCHEME == kScheme2x8) {
         // Slot j holds entry (m, k) of replica r, j = (2k + m) * REPL + r; consecutive
         // threads write consecutive slots (conflict-free), reading the same 16 B source.
-        for (int j = tid; j < kCbSlots; j += kGemvThreads) {
+        // All loads first (one L2 round trip), then the LDS writes.
+        constexpr int kFill = (kCbSlots + kGemvThreads - 1) / kGemvThreads;
+        u32x4 fv[kFill];
+#pragma unroll
+        for (int it = 0; it < kFill; ++it) {
+            const int j = min(it * kGemvThreads + tid, kCbSlots - 1);
             const int km = j / REPL;
-            const int m = km & 1, k = km >> 1;
-            smem[j] = load16(codebooks + (size_t)(m * kCodewords2x8 + k) * kGroup);
+            fv[it] = load16(codebooks + (size_t)((km & 1) * kCodewords2x8 + (km >> 1)) * kGroup);
+        }
+#pragma unroll
+        for (int it = 0; it < kFill; ++it) {
+            const int j = it * kGemvThreads + tid;
+            if (j < kCbSlots) smem[j] = fv[it];
         }
     }
     __syncthreads();
@@ -154,14 +190,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
                                    : u32x4{0u, 0u, 0u, 0u};
                 }
             }
-            f16x8 bx[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int grp = g0 + q;
-                bx[q] = (lrow < T && grp < G)
-                            ? as_f16x8(load16(x + (size_t)lrow * in + (size_t)grp * kGroup))
-                            : f16x8{};
-            }
+            if (s != s_loaded) { load_x(s); s_loaded = s; }
             const uint32_t gmask = (G - g0 >= 8) ? 0xffu : (G > g0 ? (1u << (G - g0)) - 1u : 0u);
 #pragma unroll
             for (int i = 0; i < RTP; ++i) {
@@ -193,6 +222,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
             }
         }
     }
+    // Keeps the L2 warm-up loads alive; the condition never holds (tid < 1024).
+    if ((warm[0] ^ warm[3]) == 0x9e3779b9u && tid == 0xffff) y[0] = (f16)0.f;
 }
 
 template <int SCHEME, int REPL, bool VEC, int RTP>
