@@ -193,6 +193,27 @@ def spot_check(torch, E, ls: LayerSet, rows_per_layer=32):
     return worst
 
 
+def recorded_traffic():
+    """Per-launch HBM bytes of gemv_kernel<1x16> from the committed rocprofv3 PMC record.
+
+    Returned only while the kernel sources hash to the value recorded with the
+    counters; a changed kernel reports None until the counters are taken again.
+    """
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    rec_path = os.path.join(root, "profiles", "gemv_1x16_llama2_7b_block_b1_traffic.json")
+    try:
+        rec = json.load(open(rec_path))
+        h = hashlib.sha256()
+        for f in ("gemv.hip", "aqlm_device.h"):
+            h.update(open(os.path.join(root, "extreme_weight_quantization_amd", "csrc", f), "rb").read())
+        if h.hexdigest()[:16] != rec["source_sha256_16"]:
+            return None
+        return rec["per_launch_traffic_bytes_mean"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(seconds_hint=True):
     """The CPU oracle (decode in fp32, float64 product) on one of each 7B layer shape, 1x16, batch 1."""
     from extreme_weight_quantization_amd import synth
@@ -316,6 +337,24 @@ def main():
             nbytes = 4096 * 4096 // 4 + 2 * 4096 + 2 * 4096 * 4096
             dc[f"{scheme}_4096x4096"] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
         breakdown["decode"] = dc
+        # fp16 comparator (torch.matmul on dense fp16 weights: the vendor BLAS), the
+        # denominator of the "speedup vs FP16" figures the AQLM pages quote.
+        cmp16 = {}
+        aq1 = {k: v["us"] for k, v in per_shape.items()}
+        aq2 = breakdown["gemv_2x8_b1_7b_block"]["per_shape"]
+        for out, n_in in SHAPES_7B:
+            n = max(2, min(32, -(-LLC_BYTES * 2 // (2 * out * n_in))))
+            ws16 = [torch.randn((out, n_in), generator=gen, device="cuda", dtype=torch.float32).half()
+                    for _ in range(n)]
+            xv = make_x(torch, 1, n_in, gen)
+            us16 = time_calls(torch, lambda i: torch.matmul(xv, ws16[i % n].t()), 4 * n, 2)
+            key = f"{out}x{n_in}"
+            cmp16[key] = {"fp16_us": round(us16, 3),
+                          "speedup_1x16": round(us16 / aq1[key], 3),
+                          "speedup_2x8": round(us16 / aq2[key]["us"], 3)}
+            del ws16
+            torch.cuda.empty_cache()
+        breakdown["gemv_b1_vs_fp16"] = cmp16
 
     if args.copy_probe:
         src = torch.empty(32 << 20, dtype=torch.float16, device="cuda").normal_()
@@ -351,7 +390,7 @@ def main():
             "device": dev_name,
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": "gemv_kernel<1x16>", "kernel_us_per_step": round(kern_us_step, 3),
                      "method": "per-shape mean duration of back-to-back launches replayed from a HIP graph"},
         "cpu_baseline": cpu,
