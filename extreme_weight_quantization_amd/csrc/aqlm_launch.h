@@ -15,6 +15,11 @@ hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, con
                        const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                        hipStream_t stream);
 
+// 2x8 prefill product with the role-split pipeline; requires in % 64 == 0.
+hipError_t launch_gemm_pipe_2x8(const void* codes, const void* codebooks, const void* scales,
+                                const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                                hipStream_t stream);
+
 hipError_t launch_gemm(int scheme, const void* codes, const void* codebooks, const void* scales,
                        const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                        hipStream_t stream);

@@ -18,6 +18,9 @@
 // step earlier than they are written, from codes loaded one step before that.
 // Consecutive workgroups take consecutive token tiles of one W tile, so with
 // 8 token tiles every XCD keeps one X tile in its L2.
+//
+// This is the general kernel (any in % 8 == 0, both schemes).  The 2x8 scheme
+// with in % 64 == 0 takes the role-split pipeline of gemm_pipe.hip instead.
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
@@ -245,8 +248,11 @@ hipError_t launch_gemm_t(const void* codes, const void* codebooks, const void* s
 hipError_t launch_gemm(int scheme, const void* codes, const void* codebooks, const void* scales,
                        const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                        hipStream_t stream) {
-    if (scheme == kScheme2x8)
+    if (scheme == kScheme2x8) {
+        if (in % 64 == 0)
+            return launch_gemm_pipe_2x8(codes, codebooks, scales, x, y, out, in, batch, stream);
         return launch_gemm_t<kScheme2x8, 256, 128, 4, 2, 2>(codes, codebooks, scales, x, y, out, in, batch, stream);
+    }
     return launch_gemm_t<kScheme1x16, 256, 128, 4, 2, 1>(codes, codebooks, scales, x, y, out, in, batch, stream);
 }
 

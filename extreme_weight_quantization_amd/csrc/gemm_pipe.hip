@@ -1,0 +1,262 @@
+// Prefill product for the 2x8 scheme with a role-split software pipeline:
+//   Y[t][i] = s[i] * sum_k X[t][k] Wc[i][k],  Wc[i][8j+u] = C0[b0][u] + C1[b1][u].
+//
+// "The AQLM Quantization Algorithm, Explained", Figure 2 of the MCQ section:
+// the product runs on dequantized half-precision weights, each built from one
+// codeword per codebook.  This kernel is the fast path for in % 64 == 0; the
+// general kernel in gemm.hip handles every other shape.
+//
+// A workgroup owns a 256-token x 128-row output tile and walks k in steps of
+// 64 inputs (8 groups).  Each step is split into two k-halves of 32 inputs.
+// Twelve waves play two roles:
+//
+//   8 consumer waves  each own a 64x64 piece of the tile.  They copy X
+//                     straight from global memory into LDS (direct-to-LDS
+//                     loads), read 16-byte fragments and run 16x16x32 fp16
+//                     matrix-core products with fp32 accumulators.
+//   4 producer waves  stream the codes of the tile far ahead into an LDS ring
+//                     (also direct-to-LDS) and decode W from the LDS copy of
+//                     the two codebooks into LDS as fp16.
+//
+// Only code loads go through the producers' vector-memory counter, so they can
+// run kRing steps ahead; the consumers' counter only holds X loads.  Both
+// counters retire in issue order, which is why the two kinds of loads live in
+// different waves.
+//
+// Pipeline (one barrier per step; B_k is the barrier that ends step k):
+//   consumer step k : load X(k+3) half 0 and X(k+2) half 1;
+//                     read half 1 of step k, multiply half 0 of step k;
+//                     read half 0 of step k+1, multiply half 1 of step k;
+//                     B_k waits for every X load issued before step k.
+//   producer step k : load the codes of step k+kRing;
+//                     decode W(k+2) half 0 and W(k+1) half 1;
+//                     B_k waits for the codes of step k+3.
+// Every X half thus has two steps to arrive, every code load about kRing-3.
+// X keeps three stages, W two (a W half is written one step before it is
+// read), the code ring kRing steps: 96 + 32 + 24 + 8 (codebooks) = 160 KB.
+//
+// LDS layout of one k-half of a tile: row r holds 4 chunks of 16 bytes; chunk c
+// sits in slot 4r + (c ^ ((r >> 2) & 3)).  A direct-to-LDS load writes 64
+// consecutive slots (16 whole rows), and the 16 lanes of a fragment read hit
+// 16 distinct bank groups.
+#include "aqlm_device.h"
+#include "aqlm_launch.h"
+
+namespace aqlm {
+
+namespace {
+
+constexpr int kPipeBM = 256;                 // tokens per tile
+constexpr int kPipeBN = 128;                 // output rows per tile
+constexpr int kPipeConsumers = 8;            // consumer waves
+constexpr int kPipeProducers = 4;            // producer waves
+constexpr int kPipeThreads = 64 * (kPipeConsumers + kPipeProducers);
+constexpr int kPipeXHalf = kPipeBM * 4;      // 16-byte slots of one X k-half
+constexpr int kPipeWHalf = kPipeBN * 4;      // 16-byte slots of one W k-half
+constexpr int kPipeWStages = 2;
+constexpr int kPipeRing = 12;                // steps of codes held in LDS
+constexpr int kPipeCb = 2 * kCodewords2x8;   // codebook slots: codeword k of codebook m at 2k+m
+constexpr int kPipeXOff = 0;
+constexpr int kPipeWOff = kPipeXOff + 3 * 2 * kPipeXHalf;
+constexpr int kPipeRingOff = kPipeWOff + kPipeWStages * 2 * kPipeWHalf;
+constexpr int kPipeCbOff = kPipeRingOff + kPipeRing * kPipeBN;
+constexpr size_t kPipeLds = (size_t)(kPipeCbOff + kPipeCb) * 16;
+static_assert(kPipeLds <= 163840, "LDS budget");
+
+// s_waitcnt lgkmcnt(0) with the vector-memory and export counters left at their maxima
+constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
+
+__device__ __forceinline__ int half_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
+    return (__attribute__((address_space(3))) void*)p;
+}
+
+__global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
+    const uint8_t* __restrict__ codes, const f16* __restrict__ codebooks,
+    const f16* __restrict__ scales, const f16* __restrict__ x, f16* __restrict__ y,
+    int out, int in, int T) {
+    extern __shared__ u32x4 smem[];
+    u32x4* Xs = smem + kPipeXOff;       // [stage 3][half 2][kPipeXHalf]
+    u32x4* Ws = smem + kPipeWOff;       // [stage 2][half 2][kPipeWHalf]
+    u32x4* ring = smem + kPipeRingOff;  // [kPipeRing][row 128] : the 8 group codes of a row, 16 bytes
+    u32x4* cb = smem + kPipeCbOff;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = in / kGroup;
+    const int n_k = G / 8;                          // the launcher guarantees in % 64 == 0
+    const int n_tt = (T + kPipeBM - 1) / kPipeBM;
+    const int n0 = (int)(blockIdx.x / n_tt) * kPipeBN;
+    const int t0 = (int)(blockIdx.x % n_tt) * kPipeBM;
+
+    for (int j = tid; j < kPipeCb; j += kPipeThreads)
+        cb[j] = load16(codebooks + (size_t)((j & 1) * kCodewords2x8 + (j >> 1)) * kGroup);
+
+    if (wave >= kPipeConsumers) {
+        // ------------------------------ producers ------------------------------
+        const int pw = wave - kPipeConsumers;
+        const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
+        // the 2 KB of codes of step j: dword d of the slot is dword d & 3 of row d >> 2
+        auto load_codes = [&](int j) {
+            const int jc = min(j, n_k - 1);
+            uint32_t* slot = reinterpret_cast<uint32_t*>(ring + (j % kPipeRing) * kPipeBN);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int d = (2 * pw + i) * 64 + lane;
+                const int row = min(n0 + (d >> 2), out - 1);
+                __builtin_amdgcn_global_load_lds((const void*)(c32 + (size_t)row * (G / 2) + jc * 4 + (d & 3)),
+                                                 lds_ptr(slot + (2 * pw + i) * 64), 4, 0, 0);
+            }
+        };
+        // thread p decodes chunks c0, c0+1 of row r in one half of each of two steps;
+        // every LDS read is issued before the first write so the lookups overlap
+        const int p = tid - 64 * kPipeConsumers;
+        const int r = p >> 1, c0 = 2 * (p & 1);
+        auto decode2 = [&](int ja, int ha, int jb, int hb) {
+            const uint32_t ca = reinterpret_cast<const uint32_t*>(ring + (ja % kPipeRing) * kPipeBN + r)[(4 * ha + c0) >> 1];
+            const uint32_t cw = reinterpret_cast<const uint32_t*>(ring + (jb % kPipeRing) * kPipeBN + r)[(4 * hb + c0) >> 1];
+            f16x8 e[8];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                e[2 * q] = as_f16x8(cb[2 * ((ca >> (16 * q)) & 0xff)]);
+                e[2 * q + 1] = as_f16x8(cb[2 * ((ca >> (16 * q + 8)) & 0xff) + 1]);
+                e[4 + 2 * q] = as_f16x8(cb[2 * ((cw >> (16 * q)) & 0xff)]);
+                e[5 + 2 * q] = as_f16x8(cb[2 * ((cw >> (16 * q + 8)) & 0xff) + 1]);
+            }
+            u32x4* da = Ws + ((ja % kPipeWStages) * 2 + ha) * kPipeWHalf;
+            u32x4* db = Ws + ((jb % kPipeWStages) * 2 + hb) * kPipeWHalf;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                da[half_slot(r, c0 + q)] = as_u32x4(e[2 * q] + e[2 * q + 1]);
+                db[half_slot(r, c0 + q)] = as_u32x4(e[4 + 2 * q] + e[5 + 2 * q]);
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < kPipeRing; ++j) load_codes(j);
+        // P1: codebook copy staged, codes of steps 0 and 1 landed
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kPipeRing - 2)) : "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        decode2(0, 0, 0, 1);
+        decode2(1, 0, 1, 0);
+        // P2: W(0), W(1) half 0 written, codes of step 2 landed
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kPipeRing - 3)) : "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        for (int k = 0; k + 1 < n_k; ++k) {
+            load_codes(k + kPipeRing);          // replaces step k's codes, last read before B_{k-1}
+            __builtin_amdgcn_sched_barrier(0);
+            decode2(k + 2, 0, k + 1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // B_k: W written, codes of step k+3 landed (issued kPipeRing-3 steps ago or earlier)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kPipeRing - 3)) : "memory");
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load in flight at exit
+        return;
+    }
+
+    // ------------------------------ consumers ------------------------------
+    const int wm = wave >> 1, wn = wave & 1;
+    // X half h of step j into stage j % 3: this wave writes rows 32*wave .. 32*wave+31
+    auto load_x = [&](int j, int h) {
+        const int jc = min(j, n_k - 1);
+        u32x4* dst = Xs + ((j % 3) * 2 + h) * kPipeXHalf;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = 2 * wave + i;                     // 16 rows per direct load
+            const int rr = 16 * q + (lane >> 2);
+            const int c = (lane & 3) ^ ((lane >> 4) & 3);   // slot 4*rr + (lane & 3) holds chunk c
+            const int tok = min(t0 + rr, T - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)tok * in + (size_t)(8 * jc + 4 * h + c) * kGroup),
+                                             lds_ptr(dst + 64 * q), 16, 0, 0);
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fragments of half h of step j: lane l holds A[l%16][8(l/16)..] and B[8(l/16)..][l%16]
+    auto read_frags = [&](int j, int h, f16x8 (&a)[4], f16x8 (&b)[4]) {
+        const u32x4* xb = Xs + ((j % 3) * 2 + h) * kPipeXHalf;
+        const u32x4* wb = Ws + ((j % kPipeWStages) * 2 + h) * kPipeWHalf;
+        const int c = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = as_f16x8(xb[half_slot(wm * 64 + i * 16 + (lane & 15), c)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = as_f16x8(wb[half_slot(wn * 64 + i * 16 + (lane & 15), c)]);
+    };
+    // 16 products of one k-half, one fragment read slotted between every two of them
+    auto mma16 = [&](const f16x8 (&a)[4], const f16x8 (&b)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two matrix products
+        }
+    };
+    load_x(0, 0);
+    load_x(0, 1);
+    load_x(1, 0);
+    load_x(1, 1);
+    load_x(2, 0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // P1: codebook copy staged
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");     // P2: X(0), X(1), X(2) half 0 landed
+    f16x8 a0[4], b0[4], a1[4], b1[4];
+    read_frags(0, 0, a0, b0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    auto step = [&](int k) {
+        load_x(k + 3, 0);   // stage k%3 half 0: step k's half 0 was read before B_{k-1}
+        load_x(k + 2, 1);   // stage (k+2)%3 half 1: step k-1's half 1 was read before B_{k-1}
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(k, 1, a1, b1);
+        mma16(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(min(k + 1, n_k - 1), 0, a0, b0);
+        mma16(a1, b1);
+    };
+    for (int k = 0; k + 1 < n_k; ++k) {
+        step(k);
+        __builtin_amdgcn_sched_barrier(0);
+        // B_k: the four X loads of this step stay in flight, all earlier ones have landed
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    }
+    // The last step's half-0 read of step n_k-1 is dead and may race with its own X loads.
+    step(n_k - 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load in flight at exit
+
+    // epilogue: lane holds D[4*(l/16)+r][l%16] of block (i, j)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
+        if (col >= out) continue;
+        const float s = (float)scales[col];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int tok = t0 + wm * 64 + i * 16 + 4 * (lane >> 4) + rr;
+                if (tok < T) y[(size_t)tok * out + col] = (f16)(acc[i][j][rr] * s);
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_pipe_2x8(const void* codes, const void* codebooks, const void* scales,
+                                const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                                hipStream_t stream) {
+    if (in % 64 != 0) return hipErrorInvalidValue;
+    const hipError_t e = hipFuncSetAttribute((const void*)gemm_pipe_2x8_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPipeLds);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)(((out + kPipeBN - 1) / kPipeBN) * ((batch + kPipeBM - 1) / kPipeBM)));
+    hipLaunchKernelGGL(gemm_pipe_2x8_kernel, grid, dim3(kPipeThreads), kPipeLds, stream,
+                       (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales, (const f16*)x,
+                       (f16*)y, (int)out, (int)in, (int)batch);
+    return hipGetLastError();
+}
+
+}  // namespace aqlm

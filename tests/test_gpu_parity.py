@@ -233,6 +233,8 @@ def run_gemm(layer):
     (300, 4160, 130),   # several tiles, ragged tails
     (128, 256, 256),
     (17, 8, 3),
+    (200, 64, 70),      # a single k-step
+    (1000, 1024, 513),  # 2x8 pipelined path: several row and token tiles, ragged
 ])
 def test_gemm_small(scheme, out, n_in, batch):
     L = synth.make_layer(scheme, out, n_in, batch=batch, seed=0)
@@ -241,17 +243,20 @@ def test_gemm_small(scheme, out, n_in, batch):
 
 
 @pytest.mark.parametrize("scheme", ["2x8", "1x16"])
-def test_gemm_basis_exact(scheme):
-    """X = identity rows: Y equals W16 transposed exactly with dyadic one-hot codebooks."""
+@pytest.mark.parametrize("n_in", [136, 192])
+def test_gemm_basis_exact(scheme, n_in):
+    """X = identity rows: Y equals W16 transposed exactly with dyadic one-hot codebooks.
+
+    in = 136 runs the general kernel, in = 192 (a multiple of 64) the 2x8 pipelined one."""
     M, B, g, _ = synth.SCHEMES[scheme]
     cb = np.zeros((M, 1 << B, g), np.float16)
     k = np.arange(1 << B)
     for m in range(M):
         cb[m, k, k % 8] = (2.0 ** -(m + 1)) * (((k >> 3) % 32) + 1) / 32
-    L = synth.make_layer(scheme, 72, 136, batch=136, seed=3)
+    L = synth.make_layer(scheme, 72, n_in, batch=n_in, seed=3)
     L.codebooks = cb
     L.scales = np.random.default_rng(1).choice([0.5, 1.0, 2.0], size=72).astype(np.float16)
-    L.x = np.eye(136, dtype=np.float16)
+    L.x = np.eye(n_in, dtype=np.float16)
     y = run_gemm(L)
     np.testing.assert_array_equal(y, O.decode_fp16(L.codes, L.codebooks, L.scales).astype(np.float64).T)
 
