@@ -140,6 +140,37 @@ def gemv_launches(E, ls, k0, n_steps, only=None):
     return out
 
 
+# The 7B block's layers that multiply the same activations: q, k, v | o | gate, up | down.
+BLOCK_7B_GROUPS = ((0, 1, 2), (3,), (4, 5), (6,))
+
+
+def fused_block_launches(E, ls, k0, n_steps):
+    """One pass over the block per step with the projections that share x fused into one launch."""
+    out = []
+    for k in range(k0, k0 + n_steps):
+        layers = ls.sets[k % len(ls.sets)]
+        for grp in BLOCK_7B_GROUPS:
+            x = layers[grp[0]][2]
+            if len(grp) == 1:
+                codes, s, _, y = layers[grp[0]]
+                out.append(lambda c=codes, s=s, x=x, y=y: E.aqlm_linear_gemv(c, ls.cb, s, x, y))
+            else:
+                lay = [(layers[i][0], ls.cb, layers[i][1]) for i in grp]
+                ys = [layers[i][3] for i in grp]
+                out.append(lambda lay=lay, x=x, ys=ys: E.aqlm_linear_gemv_fused(lay, x, ys))
+    return out
+
+
+def time_fused_block(torch, E, ls: LayerSet, steps, warmup):
+    """ms per 7B block step with fused projections (same rotation and graph timing as time_gemv)."""
+    g_warm = capture(torch, fused_block_launches(E, ls, 0, max(1, warmup)))
+    g_main = capture(torch, fused_block_launches(E, ls, warmup, steps))
+    replay_us(torch, g_warm)
+    ms_step = replay_us(torch, g_main) / steps / 1e3
+    del g_warm, g_main
+    return ms_step
+
+
 def time_gemv(torch, E, ls: LayerSet, steps, warmup):
     """Times exactly `steps` passes over the layer list (rotating buffer sets).
 
@@ -275,6 +306,12 @@ def main():
     per_shape = {f"{o}x{i}": {"us": round(us, 3), "GBps": round(gemv_bytes(o, i, 1) / (us * 1e-6) / 1e9, 1),
                               "pct_hbm_peak": round(100 * gemv_bytes(o, i, 1) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
                  for (o, i), us in shape_us.items()}
+    fused = {}
+    if not args.quick:
+        ms_f = time_fused_block(torch, E, ls, max(20, args.steps // 2), 5)
+        fused["1x16_b1"] = {"ms_per_step": round(ms_f, 5), "us_per_layer": round(ms_f * 1e3 / len(BLOCK_7B), 3),
+                            "GBps_step": round(ls.bytes_per_step / (ms_f * 1e-3) / 1e9, 1),
+                            "unfused_ms_per_step": round(ms_step, 5)}
     del ls
     torch.cuda.empty_cache()
 
@@ -287,6 +324,11 @@ def main():
             if b == 1:
                 spot_check(torch, E, ls2)
             ms2, sh2 = time_gemv(torch, E, ls2, iters, 5)
+            ms2f = time_fused_block(torch, E, ls2, iters, 5)
+            fused[f"2x8_b{b}"] = {"ms_per_step": round(ms2f, 5),
+                                  "us_per_layer": round(ms2f * 1e3 / len(BLOCK_7B), 3),
+                                  "GBps_step": round(ls2.bytes_per_step / (ms2f * 1e-3) / 1e9, 1),
+                                  "unfused_ms_per_step": round(ms2, 5)}
             k2 = sum(sh2[sh] for sh in BLOCK_7B)
             breakdown[f"gemv_2x8_b{b}_7b_block"] = {
                 "us_per_layer": round(k2 / len(BLOCK_7B), 3),
@@ -308,6 +350,7 @@ def main():
             del ls3
             torch.cuda.empty_cache()
         breakdown["gemv_1x16_b1_70b"] = r70
+        breakdown["gemv_fused_7b_block"] = fused
         # prefill GEMM, 2048 tokens
         gen = torch.Generator(device="cuda")
         gen.manual_seed(3)

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     aqlm_linear_decode,
     aqlm_linear_gemm,
     aqlm_linear_gemv,
+    aqlm_linear_gemv_fused,
     load_library,
     status_str,
 )

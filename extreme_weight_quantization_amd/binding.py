@@ -16,8 +16,9 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaqlm.so")
 
 AQLM_OK, AQLM_ERR_NULL, AQLM_ERR_SHAPE, AQLM_ERR_SCHEME, AQLM_ERR_ALIGN, AQLM_ERR_HIP = range(6)
-EXPORTED = ("aqlm_linear_gemv", "aqlm_linear_gemm", "aqlm_linear_decode",
+EXPORTED = ("aqlm_linear_gemv", "aqlm_linear_gemv_fused", "aqlm_linear_gemm", "aqlm_linear_decode",
             "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
+FUSED_MAX_LAYERS = 8   # AQLM_FUSED_MAX_LAYERS
 
 _lib = None
 _lock = threading.Lock()
@@ -44,6 +45,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, i64, i64, i64, vp]
             fn.restype = ci
+        pp = ctypes.POINTER(vp)
+        lib.aqlm_linear_gemv_fused.argtypes = [ci, pp, pp, pp, ctypes.POINTER(i64), vp, pp,
+                                               ci, ci, ci, i64, i64, vp]
+        lib.aqlm_linear_gemv_fused.restype = ci
         lib.aqlm_status_str.argtypes = [ci]
         lib.aqlm_status_str.restype = ctypes.c_char_p
         lib.aqlm_last_hip_error.argtypes = []
@@ -126,6 +131,52 @@ def aqlm_linear_gemv(codes, codebooks, scales, x, y=None):
     return _linear("aqlm_linear_gemv", codes, codebooks, scales, x, y)
 
 
+def aqlm_linear_gemv_fused(layers, x, ys=None):
+    """[y_l] for layers l = (codes, codebooks, scales) that all multiply the same x, in one launch.
+
+    The layers share the scheme and `in`; each has its own rows.  Results equal
+    separate aqlm_linear_gemv calls bit for bit (see aqlm.h)."""
+    layers = list(layers)
+    if not 1 <= len(layers) <= FUSED_MAX_LAYERS:
+        raise ValueError(f"1 to {FUSED_MAX_LAYERS} layers per call")
+    scheme = None
+    outs = []
+    for codes, codebooks, scales in layers:
+        _check_tensors(codes, codebooks, scales, x)
+        sch = _scheme(codes, codebooks)
+        if scheme is not None and sch != scheme:
+            raise ValueError("all layers of a fused call must use the same (M, B, g)")
+        scheme = sch
+        outs.append(int(codes.shape[0]))
+    M, B, g = scheme
+    n_in = int(layers[0][0].shape[1]) * g
+    for codes, _, _ in layers:
+        if int(codes.shape[1]) * g != n_in:
+            raise ValueError("all layers of a fused call must have the same in")
+    if x.dim() != 2 or x.shape[1] != n_in:
+        raise ValueError(f"x must be [batch][{n_in}]")
+    batch = int(x.shape[0])
+    if ys is None:
+        ys = [torch.empty((batch, o), dtype=torch.float16, device=x.device) for o in outs]
+    else:
+        ys = list(ys)
+        if len(ys) != len(layers):
+            raise ValueError("one output per layer")
+        for y, o in zip(ys, outs):
+            if y.shape != (batch, o) or y.dtype != torch.float16 or not y.is_contiguous():
+                raise ValueError(f"y must be a contiguous float16 [{batch}][{o}] tensor")
+    n = len(layers)
+    arr = ctypes.c_void_p * n
+    c_codes = arr(*[l[0].data_ptr() for l in layers])
+    c_cb = arr(*[l[1].data_ptr() for l in layers])
+    c_s = arr(*[l[2].data_ptr() for l in layers])
+    c_y = arr(*[y.data_ptr() for y in ys])
+    c_out = (ctypes.c_int64 * n)(*outs)
+    _check(load_library().aqlm_linear_gemv_fused(n, c_codes, c_cb, c_s, c_out, _ptr(x), c_y,
+                                                 M, B, g, n_in, batch, _stream(x.device)))
+    return ys
+
+
 def aqlm_linear_gemm(codes, codebooks, scales, x, y=None):
     """Y = X W^T for a prefill batch of tokens (see aqlm.h)."""
     return _linear("aqlm_linear_gemm", codes, codebooks, scales, x, y)
@@ -143,6 +194,16 @@ def aqlm_linear_decode(codes, codebooks, scales, w=None):
     _check(load_library().aqlm_linear_decode(_ptr(codes), _ptr(codebooks), _ptr(scales), None,
                                              _ptr(w), M, B, g, out, G * g, 0, _stream(codes.device)))
     return w
+
+
+def raw_call_fused(n_layers, codes, codebooks, scales, outs, x, ys, M, B, g, n_in, batch, stream=0) -> int:
+    """Call aqlm_linear_gemv_fused with raw integer addresses (lists, or None for a NULL array)."""
+    def arr(vals):
+        return None if vals is None else (ctypes.c_void_p * max(len(vals), 1))(*vals)
+    c_out = None if outs is None else (ctypes.c_int64 * max(len(outs), 1))(*outs)
+    return int(load_library().aqlm_linear_gemv_fused(
+        n_layers, arr(codes), arr(codebooks), arr(scales), c_out, ctypes.c_void_p(x), arr(ys),
+        M, B, g, n_in, batch, ctypes.c_void_p(stream)))
 
 
 def raw_call(fn_name, codes, codebooks, scales, x, y, M, B, g, out, n_in, batch, stream=0) -> int:

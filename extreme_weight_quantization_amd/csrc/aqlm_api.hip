@@ -9,6 +9,8 @@
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
+static_assert(AQLM_FUSED_MAX_LAYERS == aqlm::kGemvMaxLayers, "fused layer limit");
+
 namespace aqlm {
 
 namespace {
@@ -85,6 +87,31 @@ int aqlm_linear_gemv(const void* codes, const void* codebooks, const void* scale
     if (st != AQLM_OK || empty) return st;
     return finish(launch_gemv(scheme, codes, codebooks, scales, x, y, out, in, batch,
                               (hipStream_t)stream));
+}
+
+int aqlm_linear_gemv_fused(int n_layers, const void* const* codes, const void* const* codebooks,
+                           const void* const* scales, const int64_t* outs, const void* x,
+                           void* const* ys, int M, int B, int g, int64_t in, int64_t batch,
+                           void* stream) {
+    if (n_layers < 1 || n_layers > AQLM_FUSED_MAX_LAYERS) return AQLM_ERR_SHAPE;
+    if (!codes || !codebooks || !scales || !outs || !ys) return AQLM_ERR_NULL;
+    GemvLayers layers = {};
+    int scheme = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        bool empty = false;
+        const int st = validate(Op::kGemv, codes[l], codebooks[l], scales[l], x, ys[l], M, B, g, outs[l],
+                                in, batch, &scheme, &empty);
+        if (st != AQLM_OK) return st;
+        if (empty) continue;
+        layers.codes[layers.n] = codes[l];
+        layers.codebooks[layers.n] = codebooks[l];
+        layers.scales[layers.n] = scales[l];
+        layers.y[layers.n] = ys[l];
+        layers.out[layers.n] = (int)outs[l];
+        ++layers.n;
+    }
+    if (layers.n == 0) return AQLM_OK;
+    return finish(launch_gemv_fused(scheme, layers, x, in, batch, (hipStream_t)stream));
 }
 
 int aqlm_linear_gemm(const void* codes, const void* codebooks, const void* scales, const void* x,

@@ -11,6 +11,25 @@ int device_cu_count();
 hipError_t launch_decode(int scheme, const void* codes, const void* codebooks, const void* scales,
                          void* w, int64_t out, int64_t in, hipStream_t stream);
 
+// Layers of one GEMV launch: every layer has its own codes, codebooks, scales,
+// y and out, and all of them share x, in, batch and the scheme.  Workgroups
+// [wg_end[l-1], wg_end[l]) serve layer l (wg_end[-1] = 0); the launcher fills
+// wg_end.  Passed to the kernel by value.
+constexpr int kGemvMaxLayers = 8;
+struct GemvLayers {
+    const void* codes[kGemvMaxLayers];
+    const void* codebooks[kGemvMaxLayers];
+    const void* scales[kGemvMaxLayers];
+    void* y[kGemvMaxLayers];
+    int out[kGemvMaxLayers];
+    int wg_end[kGemvMaxLayers];
+    int n;
+};
+
+// Several layers that share x in one launch (layers with out == 0 must be left out).
+hipError_t launch_gemv_fused(int scheme, GemvLayers layers, const void* x, int64_t in,
+                             int64_t batch, hipStream_t stream);
+
 hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, const void* scales,
                        const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                        hipStream_t stream);

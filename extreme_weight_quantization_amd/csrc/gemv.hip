@@ -9,7 +9,8 @@
 //
 // Work decomposition (one workgroup of 16 waves per CU):
 //  * rows are cut into tiles of 16 (the M side of a 16x16x32 fp16 matrix-core
-//    product); a workgroup owns row tiles blockIdx.x, +gridDim.x, ...
+//    product); workgroup w of the W workgroups of a layer owns its row tiles
+//    w, w + W, w + 2W, ...
 //  * the input dimension is cut into slabs of 32 groups (256 inputs); the
 //    waves of a workgroup take slabs round-robin, and for each slab keep the
 //    activation operand (x, batch padded to 16 columns) in registers while
@@ -22,6 +23,14 @@
 //    groups; 1x16 codewords are gathered from the L2-resident 1 MiB codebook;
 //  * per-wave partial tiles are summed in LDS; the row scale is applied once
 //    in fp32 and y is rounded to fp16.
+//
+// One launch can serve several layers that share x (the q, k and v
+// projections of an attention block, the gate and up projections of its
+// MLP): each workgroup belongs to one layer, whose codebooks it stages, and
+// walks that layer's row tiles exactly as a launch for that layer alone
+// would, so the results are bit-identical to separate launches.  The launch
+// and the first-load, codebook-staging and reduction latencies are then paid
+// once per group of layers instead of once per layer.
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
@@ -91,12 +100,22 @@ __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restr
 }
 
 template <int SCHEME, int REPL, bool VEC, int RTP>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __restrict__ codes,
-                                                            const f16* __restrict__ codebooks,
-                                                            const f16* __restrict__ scales,
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvLayers L,
                                                             const f16* __restrict__ x,
-                                                            f16* __restrict__ y,
-                                                            int out, int in, int T) {
+                                                            int in, int T) {
+    // This workgroup's layer: the number of layer ends at or below blockIdx.x.
+    int li = 0;
+#pragma unroll
+    for (int i = 0; i + 1 < kGemvMaxLayers; ++i) li += (i + 1 < L.n && (int)blockIdx.x >= L.wg_end[i]) ? 1 : 0;
+    const int wg0 = li > 0 ? L.wg_end[li > 0 ? li - 1 : 0] : 0;
+    const int bid = (int)blockIdx.x - wg0;     // workgroup index within the layer
+    const int nwg = L.wg_end[li] - wg0;        // workgroups of the layer
+    const uint8_t* __restrict__ codes = static_cast<const uint8_t*>(L.codes[li]);
+    const f16* __restrict__ codebooks = static_cast<const f16*>(L.codebooks[li]);
+    const f16* __restrict__ scales = static_cast<const f16*>(L.scales[li]);
+    f16* __restrict__ y = static_cast<f16*>(L.y[li]);
+    const int out = L.out[li];
+
     extern __shared__ u32x4 smem[];
     constexpr int kCbSlots = (SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0;
     float* red = reinterpret_cast<float*>(smem + kCbSlots);
@@ -114,12 +133,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
 
     // First codes and activations of this wave, issued before the codebook is
     // staged so that their memory latency overlaps the LDS fill.
-    int rt0 = blockIdx.x;
+    int rt0 = bid;
     int s0 = wave;
     u32x4 cnext[RTP];
 #pragma unroll
     for (int i = 0; i < RTP; ++i) {
-        const int rt = rt0 + i * (int)gridDim.x;
+        const int rt = rt0 + i * nwg;
         cnext[i] = (s0 < n_slab && rt < n_rt)
                        ? load_codes<VEC>(codes, rt * kRowTile + lrow, out, s0 * kSlabGroups + kq * 8, G)
                        : u32x4{0u, 0u, 0u, 0u};
@@ -168,7 +187,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
     }
     __syncthreads();
 
-    for (; rt0 < n_rt; rt0 += gridDim.x * RTP) {
+    for (; rt0 < n_rt; rt0 += nwg * RTP) {
         f32x4 acc[RTP];
 #pragma unroll
         for (int i = 0; i < RTP; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -181,10 +200,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
             // Prefetch the codes of this wave's next slab (or of the next pass).
             {
                 int sn = s + kGemvWaves, rtn = rt0;
-                if (sn >= n_slab) { sn = wave; rtn = rt0 + (int)gridDim.x * RTP; }
+                if (sn >= n_slab) { sn = wave; rtn = rt0 + nwg * RTP; }
 #pragma unroll
                 for (int i = 0; i < RTP; ++i) {
-                    const int rt = rtn + i * (int)gridDim.x;
+                    const int rt = rtn + i * nwg;
                     cnext[i] = (sn < n_slab && rt < n_rt)
                                    ? load_codes<VEC>(codes, rt * kRowTile + lrow, out, sn * kSlabGroups + kq * 8, G)
                                    : u32x4{0u, 0u, 0u, 0u};
@@ -194,7 +213,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
             const uint32_t gmask = (G - g0 >= 8) ? 0xffu : (G > g0 ? (1u << (G - g0)) - 1u : 0u);
 #pragma unroll
             for (int i = 0; i < RTP; ++i) {
-                const int rt = rt0 + i * (int)gridDim.x;
+                const int rt = rt0 + i * nwg;
                 if (rt >= n_rt) break;
                 const uint32_t ok = (rt * kRowTile + lrow < out) ? gmask : 0u;
                 acc[i] = chunk_mfma<SCHEME, REPL>(ccur[i], smem, codebooks, rrep, ok, bx, acc[i]);
@@ -204,7 +223,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
         // Sum the per-wave partial tiles, scale, round to fp16.
 #pragma unroll
         for (int i = 0; i < RTP; ++i) {
-            const int rt = rt0 + i * (int)gridDim.x;
+            const int rt = rt0 + i * nwg;
             if (rt >= n_rt) break;
             __syncthreads();
 #pragma unroll
@@ -227,9 +246,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __res
 }
 
 template <int SCHEME, int REPL, bool VEC, int RTP>
-static hipError_t launch_gemv_t(const void* codes, const void* codebooks, const void* scales,
-                                const void* x, void* y, int out, int in, int T, int grid,
-                                hipStream_t stream) {
+static hipError_t launch_gemv_t(const GemvLayers& layers, const void* x, int in, int T, hipStream_t stream) {
     auto kern = gemv_kernel<SCHEME, REPL, VEC, RTP>;
     const size_t lds = (size_t)((SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0) * 16 +
                        (size_t)kGemvWaves * kRedFloats * sizeof(float);
@@ -238,27 +255,69 @@ static hipError_t launch_gemv_t(const void* codes, const void* codebooks, const 
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemvThreads), lds, stream,
-                       (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales,
-                       (const f16*)x, (f16*)y, out, in, T);
+    hipLaunchKernelGGL(kern, dim3(layers.wg_end[layers.n - 1]), dim3(kGemvThreads), lds, stream,
+                       layers, (const f16*)x, in, T);
     return hipGetLastError();
+}
+
+// Deals at most one workgroup per compute unit to the layers: a layer with
+// n_rt row tiles and w workgroups costs ceil(n_rt / w) tile passes, and each
+// further workgroup goes to the layer that costs most (a single layer gets
+// min(n_rt, CUs) workgroups).
+static void deal_workgroups(GemvLayers& layers, int cus) {
+    int w[kGemvMaxLayers], n_rt[kGemvMaxLayers];
+    int total = 0;
+    for (int l = 0; l < layers.n; ++l) {
+        n_rt[l] = (layers.out[l] + kRowTile - 1) / kRowTile;
+        w[l] = 1;
+        ++total;
+    }
+    while (total < cus) {
+        int best = -1, best_cost = 1;
+        for (int l = 0; l < layers.n; ++l) {
+            const int cost = (n_rt[l] + w[l] - 1) / w[l];
+            if (cost > best_cost || (cost == best_cost && best >= 0 && n_rt[l] > n_rt[best])) {
+                best = l;
+                best_cost = cost;
+            }
+        }
+        if (best < 0) break;   // every layer already has one workgroup per row tile
+        ++w[best];
+        ++total;
+    }
+    int end = 0;
+    for (int l = 0; l < layers.n; ++l) {
+        end += w[l];
+        layers.wg_end[l] = end;
+    }
+}
+
+hipError_t launch_gemv_fused(int scheme, GemvLayers layers, const void* x, int64_t in,
+                             int64_t batch, hipStream_t stream) {
+    constexpr int RTP = 2;
+    if (layers.n < 1) return hipSuccess;
+    deal_workgroups(layers, device_cu_count());
+    const bool vec = (in % 64) == 0;   // 16-byte aligned code rows
+    const int n = (int)in, T = (int)batch;
+    if (scheme == kScheme2x8) {
+        return vec ? launch_gemv_t<kScheme2x8, 16, true, RTP>(layers, x, n, T, stream)
+                   : launch_gemv_t<kScheme2x8, 16, false, RTP>(layers, x, n, T, stream);
+    }
+    return vec ? launch_gemv_t<kScheme1x16, 1, true, RTP>(layers, x, n, T, stream)
+               : launch_gemv_t<kScheme1x16, 1, false, RTP>(layers, x, n, T, stream);
 }
 
 hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, const void* scales,
                        const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                        hipStream_t stream) {
-    constexpr int RTP = 2;
-    const int n_rt = (int)((out + kRowTile - 1) / kRowTile);
-    const int cus = device_cu_count();
-    const int grid = n_rt < cus ? n_rt : cus;
-    const bool vec = (in % 64) == 0;   // 16-byte aligned code rows
-    const int o = (int)out, n = (int)in, T = (int)batch;
-    if (scheme == kScheme2x8) {
-        return vec ? launch_gemv_t<kScheme2x8, 16, true, RTP>(codes, codebooks, scales, x, y, o, n, T, grid, stream)
-                   : launch_gemv_t<kScheme2x8, 16, false, RTP>(codes, codebooks, scales, x, y, o, n, T, grid, stream);
-    }
-    return vec ? launch_gemv_t<kScheme1x16, 1, true, RTP>(codes, codebooks, scales, x, y, o, n, T, grid, stream)
-               : launch_gemv_t<kScheme1x16, 1, false, RTP>(codes, codebooks, scales, x, y, o, n, T, grid, stream);
+    GemvLayers layers = {};
+    layers.codes[0] = codes;
+    layers.codebooks[0] = codebooks;
+    layers.scales[0] = scales;
+    layers.y[0] = y;
+    layers.out[0] = (int)out;
+    layers.n = 1;
+    return launch_gemv_fused(scheme, layers, x, in, batch, stream);
 }
 
 }  // namespace aqlm

@@ -73,6 +73,34 @@ int aqlm_linear_gemv(const void* codes, const void* codebooks, const void* scale
                      const void* x, void* y, int M, int B, int g,
                      int64_t out, int64_t in, int64_t batch, void* stream);
 
+/* Most layers one aqlm_linear_gemv_fused call takes. */
+#define AQLM_FUSED_MAX_LAYERS 8
+
+/*
+ * n_layers decode-phase products that share the activations x, in one launch:
+ *
+ *     y_l[b][i] = sum_k W_l[i][k] * x[b][k]   for l < n_layers, b < batch,
+ *
+ * e.g. the q, k and v projections of an attention block, or the gate and up
+ * projections of its MLP, which all multiply the same hidden state.  Layer l
+ * has its own codes[l], codebooks[l], scales[l], outs[l] rows and output
+ * ys[l] ([batch][outs[l]]); all layers share (M, B, g), in, batch and x.
+ * codes, codebooks, scales, outs and ys are HOST arrays of n_layers entries;
+ * the pointers they hold are device pointers with the layouts above.  The
+ * library reads the arrays during the call and keeps nothing.
+ *
+ * Each layer is validated exactly as by aqlm_linear_gemv and the first
+ * failing layer's status is returned (nothing is enqueued then); a layer
+ * with outs[l] == 0 is skipped.  1 <= n_layers <= AQLM_FUSED_MAX_LAYERS
+ * (else AQLM_ERR_SHAPE); a NULL array gives AQLM_ERR_NULL.  The results are
+ * bit-identical to n_layers separate aqlm_linear_gemv calls; fusing pays the
+ * launch and the per-workgroup start-up latencies once for the group.
+ */
+int aqlm_linear_gemv_fused(int n_layers, const void* const* codes, const void* const* codebooks,
+                           const void* const* scales, const int64_t* outs, const void* x,
+                           void* const* ys, int M, int B, int g, int64_t in, int64_t batch,
+                           void* stream);
+
 /*
  * Same product for a prefill batch of `batch` >= 1 tokens (batch <= 2^31 - 1):
  * W tiles are decoded into LDS and fed to fp16 matrix cores with fp32

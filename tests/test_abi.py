@@ -105,6 +105,46 @@ def test_validation_decode(lib):
     assert call("aqlm_linear_decode", x=0, out=0) == binding.AQLM_OK
 
 
+def fused(n=3, **kw):
+    a = dict(VALID, **kw)
+    per = {k: kw.pop(k) for k in list(kw) if k.startswith("l_")}
+    lists = {}
+    for key in ("codes", "codebooks", "scales", "y"):
+        vals = [a[key]] * n
+        for (l, v) in per.get(f"l_{key}", []):
+            vals[l] = v
+        lists[key] = vals
+    outs = [a["out"]] * n
+    for (l, v) in per.get("l_out", []):
+        outs[l] = v
+    for key in ("codes", "codebooks", "scales", "y", "out"):
+        if a.get(f"null_{key}"):
+            lists[key] = None
+            if key == "out":
+                outs = None
+    return binding.raw_call_fused(n, lists["codes"], lists["codebooks"], lists["scales"], outs, a["x"],
+                                  lists["y"], a["M"], a["B"], a["g"], a["n_in"], a["batch"])
+
+
+def test_validation_gemv_fused(lib):
+    assert fused(n=0) == binding.AQLM_ERR_SHAPE
+    assert fused(n=binding.FUSED_MAX_LAYERS + 1) == binding.AQLM_ERR_SHAPE
+    for key in ("codes", "codebooks", "scales", "y", "out"):
+        assert fused(**{f"null_{key}": True}) == binding.AQLM_ERR_NULL
+    # every layer is validated like aqlm_linear_gemv; the first failure is returned
+    assert fused(l_codes=[(1, 0)]) == binding.AQLM_ERR_NULL
+    assert fused(l_scales=[(2, A + 1)]) == binding.AQLM_ERR_ALIGN
+    assert fused(l_y=[(0, A + 8)], l_codes=[(2, 0)]) == binding.AQLM_ERR_ALIGN
+    assert fused(l_out=[(1, -1)]) == binding.AQLM_ERR_SHAPE
+    assert fused(x=0) == binding.AQLM_ERR_NULL
+    assert fused(batch=17) == binding.AQLM_ERR_SHAPE
+    assert fused(M=1, B=8) == binding.AQLM_ERR_SCHEME
+    # empty layers are skipped; an all-empty call enqueues nothing
+    assert fused(out=0) == binding.AQLM_OK
+    assert fused(out=0, l_codes=[(0, 0)]) == binding.AQLM_OK
+    assert fused(batch=0) == binding.AQLM_OK
+
+
 def test_binding_rejects_cpu_tensors(lib):
     import torch
     codes = torch.zeros((4, 8, 2), dtype=torch.uint8)

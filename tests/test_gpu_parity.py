@@ -216,6 +216,52 @@ def test_gemv_accepts_given_output_and_stream():
 
 
 # --------------------------------------------------------------------------
+# Fused GEMV: several layers sharing x in one launch
+
+
+def run_fused(layers, x):
+    dl = [dev(L)[:3] for L in layers]
+    xd = torch.from_numpy(x).cuda()
+    ys = E.aqlm_linear_gemv_fused(dl, xd)
+    torch.cuda.synchronize()
+    sep = [E.aqlm_linear_gemv(c, cb, s, xd) for (c, cb, s) in dl]
+    torch.cuda.synchronize()
+    return [y.cpu().numpy() for y in ys], [y.cpu().numpy() for y in sep]
+
+
+@pytest.mark.parametrize("scheme", ["2x8", "1x16"])
+@pytest.mark.parametrize("outs,n_in,batch", [
+    ((4096, 4096, 4096), 4096, 1),        # q, k, v of a 7B attention block
+    ((4096, 4096, 4096), 4096, 16),
+    ((11008, 11008), 4096, 4),            # gate, up of a 7B MLP
+    ((100, 4096, 37, 1000), 520, 3),      # ragged rows and in, uneven layers
+    ((16,) * 8, 256, 1),                  # the most layers one call takes
+])
+def test_gemv_fused_matches_separate_and_oracle(scheme, outs, n_in, batch):
+    layers = [synth.make_layer(scheme, o, n_in, batch=batch, seed=10 + i) for i, o in enumerate(outs)]
+    x = layers[0].x
+    fused, sep = run_fused(layers, x)
+    for i, (L, yf, ys) in enumerate(zip(layers, fused, sep)):
+        np.testing.assert_array_equal(yf.view(np.uint16), ys.view(np.uint16), err_msg=f"layer {i}")
+        rows = sample_rows(L.codes.shape[0], 32)
+        ref = O.linear_ref_rows_f64(L.codes, L.codebooks, L.scales, x, rows)
+        assert_close(yf.astype(np.float64)[:, rows], ref, f"{scheme} fused layer {i}")
+
+
+def test_gemv_fused_skips_empty_layers():
+    a = synth.make_layer("2x8", 300, 512, batch=2, seed=1)
+    b = synth.make_layer("2x8", 64, 512, batch=2, seed=2)
+    xd = torch.from_numpy(a.x).cuda()
+    empty = (torch.zeros((0, 64, 2), dtype=torch.uint8, device="cuda"),
+             torch.from_numpy(b.codebooks).cuda(), torch.zeros(0, dtype=torch.float16, device="cuda"))
+    ys = E.aqlm_linear_gemv_fused([dev(a)[:3], empty, dev(b)[:3]], xd)
+    torch.cuda.synchronize()
+    assert ys[1].shape == (2, 0)
+    for L, y in ((a, ys[0]), (b, ys[2])):
+        assert_close(y.cpu().numpy().astype(np.float64), O.linear_ref_f64(L.codes, L.codebooks, L.scales, a.x), "skip")
+
+
+# --------------------------------------------------------------------------
 # GEMM
 
 
