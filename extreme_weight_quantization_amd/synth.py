@@ -49,22 +49,39 @@ class Layer:
         return self.codes.shape[1] * self.g
 
 
+def scheme_name(M: int, B: int, g: int) -> str:
+    return f"{M}x{B}g{g}"
+
+
 def make_layer(scheme: str, out: int, n_in: int, batch: int = 1, seed: int = 0,
                sigma: float | None = None) -> Layer:
-    """One synthetic quantized layer plus activations, seeded."""
+    """One synthetic quantized layer plus activations, seeded (a named scheme)."""
     M, B, g, default_sigma = SCHEMES[scheme]
+    layer = make_layer_mbg(M, B, g, out, n_in, batch, seed, default_sigma if sigma is None else sigma)
+    layer.scheme = scheme
+    return layer
+
+
+def make_layer_mbg(M: int, B: int, g: int, out: int, n_in: int, batch: int = 1, seed: int = 0,
+                   sigma: float = 0.05) -> Layer:
+    """One synthetic layer of any scheme: M codebooks of 2^B codewords of g entries.
+
+    Codes are stored in whole bytes (uint8 for B <= 8, int16 bit patterns for
+    9 <= B <= 16) and drawn uniform over the 2^B valid indices.
+    """
     if n_in % g:
         raise ValueError("in must be a multiple of g")
-    sigma = default_sigma if sigma is None else sigma
+    if not (1 <= B <= 16 and M >= 1 and g >= 1):
+        raise ValueError("need M >= 1, 1 <= B <= 16, g >= 1")
     rng = np.random.default_rng(seed)
     codebooks = rng.normal(0.0, sigma, size=(M, 1 << B, g)).astype(np.float16)
-    if B == 8:
-        codes = rng.integers(0, 256, size=(out, n_in // g, M), dtype=np.uint8)
+    if B <= 8:
+        codes = rng.integers(0, 1 << B, size=(out, n_in // g, M), dtype=np.uint8)
     else:
-        codes = rng.integers(0, 1 << 16, size=(out, n_in // g, M), dtype=np.uint16).view(np.int16)
+        codes = rng.integers(0, 1 << B, size=(out, n_in // g, M), dtype=np.uint16).view(np.int16)
     scales = rng.uniform(0.5, 1.5, size=out).astype(np.float16)
     x = rng.normal(0.0, 1.0, size=(batch, n_in)).astype(np.float16)
-    return Layer(scheme, M, B, g, codebooks, codes, scales, x)
+    return Layer(scheme_name(M, B, g), M, B, g, codebooks, codes, scales, x)
 
 
 def make_activations(n_in: int, batch: int, seed: int = 0) -> np.ndarray:

@@ -22,14 +22,18 @@ Sources (cited by page title and section):
   text extraction, so ``bits_per_weight`` re-derives it from those three
   listed items.
 * Same page, section "Key AQLM quantization parameters": when the code term
-  dominates, bits per parameter is about B*M/g.
+  dominates, bits per parameter is about B*M/g; at B = 8 the pairs (M, g) =
+  (1, 4), (2, 8), ..., (8, 32) all give 2 bits; a B that is not a multiple of
+  8 leaves unused bits in the bytes that hold each code.
 
 Readings where the pages are silent (each one listed in the design doc):
 
 * group j of row i covers columns [j*g, (j+1)*g); codes are stored
   ``[d_out][d_in/g][M]``; codebooks ``[M][2^B][g]``; scales ``[d_out]``;
-* a B=16 code held in an int16 is the bit pattern read as unsigned 0..65535;
-  a B=8 code held in a uint8 is its value;
+* a code is stored in whole bytes, uint8 for B <= 8 and int16 for
+  9 <= B <= 16 (the "unused bits" note above); its codeword index is the low B
+  bits of the stored pattern read as unsigned (a B=16 code in an int16 is
+  0..65535, a B=8 code in a uint8 is its value, higher bits are ignored);
 * the codewords are summed in fp32, codebook 0 first then m ascending, the
   running sum starting from codebook 0's codeword (not from +0.0), then
   multiplied by the fp32 scale; the fp16 weight is that fp32 value rounded to
@@ -45,8 +49,9 @@ import math
 
 import numpy as np
 
-# (M, B, g) triples the library accepts: 1x16 and 2x8 at g = 8
-# ("Key AQLM quantization parameters": XBit-MxB naming, e.g. 2Bit-1x16).
+# The two named schemes at g = 8 ("Key AQLM quantization parameters": XBit-MxB
+# naming, e.g. 2Bit-1x16).  The oracle itself decodes any (M, B, g) with
+# M >= 1, 1 <= B <= 16, g >= 1.
 SUPPORTED_SCHEMES = ((1, 16, 8), (2, 8, 8))
 
 
@@ -56,8 +61,10 @@ def _check_layer(codes, codebooks, scales):
         raise ValueError("codebooks must be float16 [M][2^B][g]")
     M, K, g = codebooks.shape
     B = int(round(math.log2(K))) if K > 0 else -1
-    if K <= 0 or (1 << B) != K:
-        raise ValueError("codebook size must be a power of two")
+    if K <= 0 or (1 << B) != K or B < 1:
+        raise ValueError("codebook size must be a power of two >= 2")
+    if M < 1 or g < 1:
+        raise ValueError("need M >= 1 codebooks of g >= 1 entries")
     if codes.ndim != 3 or codes.shape[2] != M:
         raise ValueError("codes must be [out][in/g][M]")
     if B <= 8:
@@ -65,7 +72,7 @@ def _check_layer(codes, codebooks, scales):
             raise ValueError("B <= 8 codes must be uint8")
     elif B <= 16:
         if codes.dtype not in (np.int16, np.uint16):
-            raise ValueError("B = 16 codes must be int16 (bit pattern) or uint16")
+            raise ValueError("9 <= B <= 16 codes must be int16 (bit pattern) or uint16")
     else:
         raise ValueError("B > 16 not representable")
     out, G, _ = codes.shape
@@ -74,18 +81,22 @@ def _check_layer(codes, codebooks, scales):
     return M, B, g, out, G * g
 
 
-def codes_to_index(codes: np.ndarray) -> np.ndarray:
+def codes_to_index(codes: np.ndarray, B: int | None = None) -> np.ndarray:
     """Codeword index of every stored code, as int64.
 
     A code is the position of the selected codeword inside its codebook
     (MCQ section: the one-hot vector is stored as its index).  uint8 codes are
-    their value; int16 codes are their 16-bit pattern read as unsigned.
+    their value; int16 codes are their 16-bit pattern read as unsigned.  With
+    B given, only the low B bits count (a code of B < 8 or B < 16 bits leaves
+    the rest of its bytes unused).
     """
     if codes.dtype == np.uint8 or codes.dtype == np.uint16:
-        return codes.astype(np.int64)
-    if codes.dtype == np.int16:
-        return codes.view(np.uint16).astype(np.int64)
-    raise ValueError(f"unsupported code dtype {codes.dtype}")
+        idx = codes.astype(np.int64)
+    elif codes.dtype == np.int16:
+        idx = codes.view(np.uint16).astype(np.int64)
+    else:
+        raise ValueError(f"unsupported code dtype {codes.dtype}")
+    return idx if B is None else idx & ((1 << B) - 1)
 
 
 def decode_fp32(codes, codebooks, scales, rows=None) -> np.ndarray:
@@ -99,7 +110,7 @@ def decode_fp32(codes, codebooks, scales, rows=None) -> np.ndarray:
         rows = np.asarray(rows, dtype=np.int64)
         codes = codes[rows]
         scales = scales[rows]
-    idx = codes_to_index(codes)                      # [r][G][M]
+    idx = codes_to_index(codes, B)                   # [r][G][M]
     acc = codebooks[0][idx[:, :, 0]].astype(np.float32)          # [r][G][g]
     for m in range(1, M):
         acc = acc + codebooks[m][idx[:, :, m]].astype(np.float32)
@@ -132,6 +143,7 @@ def decode_loop(codes, codebooks, scales) -> np.ndarray:
                     c = int(codes[i, j, m])
                     if codes.dtype == np.int16 and c < 0:
                         c += 1 << 16
+                    c %= 1 << B
                     v = f32(codebooks[m, c, t])
                     acc = v if acc is None else f32(acc + v)
                 w[i, j * g + t] = f32(acc * s)

@@ -70,6 +70,74 @@ def test_vectorised_matches_loops_1x16():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+GENERIC = [(1, 8, 4), (4, 8, 16), (8, 8, 32), (3, 5, 8), (1, 12, 4), (2, 16, 32)]
+
+
+def _junk_high_bits(codes, B, seed):
+    """Set the unused high bits of every stored code at random (the index is the low B bits)."""
+    rng = np.random.default_rng(seed)
+    bits = 8 if codes.dtype == np.uint8 else 16
+    if B == bits:
+        return codes.copy()
+    u = codes.view(np.uint8 if bits == 8 else np.uint16).astype(np.int64)
+    junk = rng.integers(0, 1 << (bits - B), size=u.shape) << B
+    out = (u | junk).astype(np.uint8 if bits == 8 else np.uint16)
+    return out if bits == 8 else out.view(np.int16)
+
+
+@pytest.mark.parametrize("M,B,g", GENERIC + [(1, 12, 1), (3, 5, 2)])
+def test_vectorised_matches_loops_generic(M, B, g):
+    """Gather decode = explicit loops, bit for bit, for budget-equivalent and odd schemes."""
+    L = synth.make_layer_mbg(M, B, g, 6, 4 * g * 4, seed=M * 100 + B)
+    codes = _junk_high_bits(L.codes, B, seed=7)
+    a = O.decode_fp32(codes, L.codebooks, L.scales)
+    b = O.decode_loop(codes, L.codebooks, L.scales)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,B,g", GENERIC)
+def test_index_layout_generic_spelled_codes(M, B, g):
+    """Codebook m spells its index k in entries 2m (k >> 8) and 2m+1 (k & 255), zero elsewhere.
+
+    With scale 1 the decoded group holds every code of the group exactly, so
+    decoding recovers the code array: this pins the [out][G][M] layout, which
+    codebook each of the M codes indexes, the column order j*g + t for any g,
+    and the reading that only the low B bits of a stored code count (the
+    codes carry random junk in their unused high bits).
+    """
+    K = 1 << B
+    k = np.arange(K)
+    cb = np.zeros((M, K, g), np.float16)
+    for m in range(M):
+        cb[m, :, 2 * m] = k >> 8
+        cb[m, :, 2 * m + 1] = k & 255
+    L = synth.make_layer_mbg(M, B, g, 5, 3 * g, seed=11)
+    codes = _junk_high_bits(L.codes, B, seed=12)
+    w = O.decode_fp32(codes, cb, np.ones(5, np.float16)).reshape(5, 3, g)
+    got = np.stack([256 * w[:, :, 2 * m] + w[:, :, 2 * m + 1] for m in range(M)], axis=-1).astype(np.int64)
+    want = O.codes_to_index(L.codes)      # the drawn codes, all < 2^B
+    np.testing.assert_array_equal(got, want)
+    assert np.all(w[:, :, 2 * M:] == 0)
+
+
+@pytest.mark.parametrize("M,B,g", GENERIC)
+def test_all_ones_generic_closed_form(M, B, g):
+    """All-ones codebooks: W[i][k] = M * s_i and y_i = M * s_i * sum(x) for any scheme."""
+    L = synth.make_layer_mbg(M, B, g, 7, 2 * g * 3, batch=2, seed=5)
+    cb = np.ones((M, 1 << B, g), np.float16)
+    w = O.decode_fp32(L.codes, cb, L.scales)
+    np.testing.assert_array_equal(w, np.repeat((M * L.scales.astype(np.float32))[:, None], w.shape[1], 1))
+    y = O.linear_ref_f64(L.codes, cb, L.scales, L.x)
+    want = M * L.scales.astype(np.float64)[None, :] * L.x.astype(np.float64).sum(1)[:, None]
+    np.testing.assert_allclose(y, want, rtol=1e-12)
+
+
+def test_budget_equivalent_pairs_code_bits():
+    """"Key AQLM quantization parameters": at B = 8 the pairs (1,4), (2,8), ..., (8,32) cost 2 code bits."""
+    for M, g in ((1, 4), (2, 8), (4, 16), (8, 32)):
+        assert O.bits_per_weight_terms(M, 8, g, 28672, 8192)["codes"] == 2.0
+
+
 def test_index_layout_2x8_bit_codebooks():
     """C0[k][t] = bit t of k, C1[k][t] = 2 * bit t of k: each decoded group spells out its two codes.
 

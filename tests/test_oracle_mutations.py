@@ -13,7 +13,7 @@ MUTANTS = {
     "drop_second_codebook": (
         "for m in range(1, M):\n        acc = acc + codebooks[m][idx[:, :, m]].astype(np.float32)", "pass"),
     "int16_codes_signed": (
-        "return codes.view(np.uint16).astype(np.int64)", "return codes.astype(np.int64)"),
+        "idx = codes.view(np.uint16).astype(np.int64)", "idx = codes.astype(np.int64)"),
     "sum_starts_at_plus_zero": (
         "acc = codebooks[0][idx[:, :, 0]].astype(np.float32)          # [r][G][g]\n    for m in range(1, M):",
         "acc = np.zeros(idx.shape[:2] + (g,), np.float32)\n    for m in range(0, M):"),
@@ -31,6 +31,12 @@ MUTANTS = {
         "acc = acc + codebooks[m][idx[:, :, m]].astype(np.float32)",
         "acc = (acc.astype(np.float16) + codebooks[m][idx[:, :, m]]).astype(np.float32)"),
     "bpw_scale_32bit": ("scales = d_out * 16 / n", "scales = d_out * 32 / n"),
+    "index_ignores_b_bits": (
+        "return idx if B is None else idx & ((1 << B) - 1)", "return idx"),
+    "loop_ignores_b_bits": ("                    c %= 1 << B\n", ""),
+    "codebook_m_reversed": (
+        "acc = acc + codebooks[m][idx[:, :, m]].astype(np.float32)",
+        "acc = acc + codebooks[M - m][idx[:, :, m]].astype(np.float32)"),
     "bpw_one_codebook": ("codebooks = M * (2 ** B) * g * 16 / n", "codebooks = (2 ** B) * g * 16 / n"),
 }
 
