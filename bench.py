@@ -65,6 +65,23 @@ def make_codes(torch, scheme, out, n_in, gen):
     return torch.randint(-32768, 32768, (out, n_in // g, M), generator=gen, device="cuda", dtype=torch.int16)
 
 
+def make_generic(torch, M, B, g, out, n_in, gen, sigma=0.05):
+    """Codebooks and codes of any (M, B, g): codes uniform over the 2^B indices, in whole bytes."""
+    cb = (torch.randn((M, 1 << B, g), generator=gen, device="cuda", dtype=torch.float32) * sigma).half()
+    c = torch.randint(0, 1 << B, (out, n_in // g, M), generator=gen, device="cuda", dtype=torch.int32)
+    codes = c.to(torch.uint8) if B <= 8 else c.to(torch.int16)
+    return cb, codes
+
+
+def generic_gemv_bytes(M, B, g, out, n_in, batch):
+    """Counted bytes of one GEMV of any scheme: codes (M codes of 1 or 2 bytes per group) + scales + x + y."""
+    return out * (n_in // g) * M * (1 if B <= 8 else 2) + 2 * out + 2 * n_in * batch + 2 * out * batch
+
+
+# The budget-equivalent 2-bit schemes of "Key AQLM quantization parameters" at B = 8.
+GENERIC_2BIT = ((1, 8, 4), (4, 8, 16), (8, 8, 32))
+
+
 def make_scales(torch, out, gen):
     return (torch.rand(out, generator=gen, device="cuda") + 0.5).half()
 
@@ -386,6 +403,29 @@ def main():
             nbytes = 4096 * 4096 // 4 + 2 * 4096 + 2 * 4096 * 4096
             dc[f"{scheme}_4096x4096"] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
         breakdown["decode"] = dc
+        # generic schemes (the pages' other 2-bit pairs at B = 8), 4096x4096
+        gs = {}
+        for M, B, g in GENERIC_2BIT:
+            cbg, codes = make_generic(torch, M, B, g, 4096, 4096, gen)
+            s = make_scales(torch, 4096, gen)
+            w = torch.empty((4096, 4096), dtype=torch.float16, device="cuda")
+            x1 = make_x(torch, 1, 4096, gen)
+            y1 = torch.empty((1, 4096), dtype=torch.float16, device="cuda")
+            x2 = make_x(torch, 2048, 4096, gen)
+            y2 = torch.empty((2048, 4096), dtype=torch.float16, device="cuda")
+            us_d = time_calls(torch, lambda i: E.aqlm_linear_decode(codes, cbg, s, w), 20, 3)
+            us_v = time_calls(torch, lambda i: E.aqlm_linear_gemv(codes, cbg, s, x1, y1), 50, 3)
+            us_m = time_calls(torch, lambda i: E.aqlm_linear_gemm(codes, cbg, s, x2, y2), 5, 1)
+            nb = generic_gemv_bytes(M, B, g, 4096, 4096, 1)
+            dbytes = nb - 2 * 4096 - 2 * 4096 + 2 * 4096 * 4096
+            gs[f"{M}x{B}g{g}_4096x4096"] = {
+                "decode_us": round(us_d, 2), "decode_GBps": round(dbytes / (us_d * 1e-6) / 1e9, 1),
+                "gemv_b1_us": round(us_v, 2), "gemv_b1_GBps": round(nb / (us_v * 1e-6) / 1e9, 1),
+                "gemm_2048_us": round(us_m, 1),
+                "gemm_2048_frac_mfma_peak": round(2.0 * 2048 * 4096 * 4096 / (us_m * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+            del cbg, codes, s, w, x1, y1, x2, y2
+            torch.cuda.empty_cache()
+        breakdown["generic_schemes"] = gs
         # fp16 comparator (torch.matmul on dense fp16 weights: the vendor BLAS), the
         # denominator of the "speedup vs FP16" figures the AQLM pages quote.
         cmp16 = {}

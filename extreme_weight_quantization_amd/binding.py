@@ -79,6 +79,10 @@ def _scheme(codes: torch.Tensor, codebooks: torch.Tensor):
         raise ValueError("codebooks must be [M][2^B][g]")
     M, K, g = codebooks.shape
     B = K.bit_length() - 1
+    if K != 1 << B:
+        raise ValueError("the codebook size must be a power of two")
+    if (B <= 8) != (codes.dtype == torch.uint8):
+        raise ValueError("codes must be uint8 for B <= 8 and int16 for 9 <= B <= 16")
     return int(M), int(B), int(g)
 
 

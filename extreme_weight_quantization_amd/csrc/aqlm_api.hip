@@ -35,14 +35,20 @@ enum class Op { kGemv, kGemm, kDecode };
 
 static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Host-side validation shared by the three entry points.  Returns AQLM_OK and
-// the scheme id, or an error status; touches no HIP state.
+static bool generic_scheme_ok(int M, int B, int g) {
+    return M >= 1 && M <= AQLM_MAX_CODEBOOKS && B >= 1 && B <= 16 &&
+           (g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32);
+}
+
+// Host-side validation shared by the entry points.  Returns AQLM_OK and the
+// scheme id, or an error status; touches no HIP state.
 static int validate(Op op, const void* codes, const void* codebooks, const void* scales,
                     const void* x, const void* y, int M, int B, int g, int64_t out, int64_t in,
                     int64_t batch, int* scheme, bool* empty) {
     if (op == Op::kDecode && x != nullptr) return AQLM_ERR_NULL;
     if (M == 1 && B == 16 && g == 8) *scheme = kScheme1x16;
     else if (M == 2 && B == 8 && g == 8) *scheme = kScheme2x8;
+    else if (generic_scheme_ok(M, B, g)) *scheme = kSchemeGeneric;
     else return AQLM_ERR_SCHEME;
     if (out < 0 || in < 1 || in > AQLM_MAX_IN || (in % g) != 0) return AQLM_ERR_SHAPE;
     if (out > (int64_t)INT32_MAX - 16) return AQLM_ERR_SHAPE;
@@ -85,6 +91,9 @@ int aqlm_linear_gemv(const void* codes, const void* codebooks, const void* scale
     bool empty = false;
     const int st = validate(Op::kGemv, codes, codebooks, scales, x, y, M, B, g, out, in, batch, &scheme, &empty);
     if (st != AQLM_OK || empty) return st;
+    if (scheme == kSchemeGeneric)
+        return finish(launch_gemv_generic(GenericScheme{M, B, g}, codes, codebooks, scales, x, y, out, in,
+                                          batch, (hipStream_t)stream));
     return finish(launch_gemv(scheme, codes, codebooks, scales, x, y, out, in, batch,
                               (hipStream_t)stream));
 }
@@ -111,6 +120,15 @@ int aqlm_linear_gemv_fused(int n_layers, const void* const* codes, const void* c
         ++layers.n;
     }
     if (layers.n == 0) return AQLM_OK;
+    if (scheme == kSchemeGeneric) {   // one launch per layer
+        for (int l = 0; l < layers.n; ++l) {
+            const int st = finish(launch_gemv_generic(GenericScheme{M, B, g}, layers.codes[l], layers.codebooks[l],
+                                                      layers.scales[l], x, layers.y[l], layers.out[l], in, batch,
+                                                      (hipStream_t)stream));
+            if (st != AQLM_OK) return st;
+        }
+        return AQLM_OK;
+    }
     return finish(launch_gemv_fused(scheme, layers, x, in, batch, (hipStream_t)stream));
 }
 
@@ -121,6 +139,9 @@ int aqlm_linear_gemm(const void* codes, const void* codebooks, const void* scale
     bool empty = false;
     const int st = validate(Op::kGemm, codes, codebooks, scales, x, y, M, B, g, out, in, batch, &scheme, &empty);
     if (st != AQLM_OK || empty) return st;
+    if (scheme == kSchemeGeneric)
+        return finish(launch_gemm_generic(GenericScheme{M, B, g}, codes, codebooks, scales, x, y, out, in,
+                                          batch, (hipStream_t)stream));
     return finish(launch_gemm(scheme, codes, codebooks, scales, x, y, out, in, batch,
                               (hipStream_t)stream));
 }
@@ -133,6 +154,9 @@ int aqlm_linear_decode(const void* codes, const void* codebooks, const void* sca
     bool empty = false;
     const int st = validate(Op::kDecode, codes, codebooks, scales, x, y, M, B, g, out, in, 1, &scheme, &empty);
     if (st != AQLM_OK || empty) return st;
+    if (scheme == kSchemeGeneric)
+        return finish(launch_decode_generic(GenericScheme{M, B, g}, codes, codebooks, scales, y, out, in,
+                                            (hipStream_t)stream));
     return finish(launch_decode(scheme, codes, codebooks, scales, y, out, in, (hipStream_t)stream));
 }
 
@@ -141,7 +165,7 @@ const char* aqlm_status_str(int status) {
         case AQLM_OK: return "AQLM_OK";
         case AQLM_ERR_NULL: return "AQLM_ERR_NULL: a required pointer is NULL (decode takes x == NULL)";
         case AQLM_ERR_SHAPE: return "AQLM_ERR_SHAPE: out/in/batch out of range or in % g != 0";
-        case AQLM_ERR_SCHEME: return "AQLM_ERR_SCHEME: (M, B, g) must be (1,16,8) or (2,8,8)";
+        case AQLM_ERR_SCHEME: return "AQLM_ERR_SCHEME: need 1 <= M <= 8, 1 <= B <= 16, g in {1,2,4,8,16,32}";
         case AQLM_ERR_ALIGN: return "AQLM_ERR_ALIGN: codes/codebooks/x/y need 16-byte, scales 2-byte alignment";
         case AQLM_ERR_HIP: return "AQLM_ERR_HIP: HIP runtime error at launch (see aqlm_last_hip_error)";
         default: return "unknown aqlm status";

@@ -13,7 +13,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Scheme ids used as template parameters.
-enum Scheme : int { kScheme2x8 = 0, kScheme1x16 = 1 };
+// kSchemeGeneric: any other (M, B, g), served by the kernels of generic.hip
+enum Scheme : int { kScheme2x8 = 0, kScheme1x16 = 1, kSchemeGeneric = 2 };
 
 constexpr int kGroup = 8;          // g: inputs per group
 constexpr int kWave = 64;          // CDNA wavefront width

@@ -8,6 +8,21 @@ namespace aqlm {
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// A scheme other than 1x16 and 2x8 at g = 8: 1 <= M <= 8, 1 <= B <= 16,
+// g in {1, 2, 4, 8, 16, 32}; codes are uint8 for B <= 8, else 16-bit.
+struct GenericScheme {
+    int M, B, g;
+};
+
+hipError_t launch_decode_generic(const GenericScheme& sc, const void* codes, const void* codebooks,
+                                 const void* scales, void* w, int64_t out, int64_t in, hipStream_t stream);
+hipError_t launch_gemv_generic(const GenericScheme& sc, const void* codes, const void* codebooks,
+                               const void* scales, const void* x, void* y, int64_t out, int64_t in,
+                               int64_t batch, hipStream_t stream);
+hipError_t launch_gemm_generic(const GenericScheme& sc, const void* codes, const void* codebooks,
+                               const void* scales, const void* x, void* y, int64_t out, int64_t in,
+                               int64_t batch, hipStream_t stream);
+
 hipError_t launch_decode(int scheme, const void* codes, const void* codebooks, const void* scales,
                          void* w, int64_t out, int64_t in, hipStream_t stream);
 

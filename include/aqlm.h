@@ -11,13 +11,19 @@
  *
  *     W[i][j*g + t] = s[i] * sum_{m=0}^{M-1} C_m[ code[i][j][m] ][t]
  *
- * Supported schemes (named XBit-MxB on the same page, section "Key AQLM
- * quantization parameters"): (M, B, g) = (1, 16, 8) "1x16" and (2, 8, 8)
- * "2x8", both 2 bits per weight in the codes.
+ * Schemes ("Key AQLM quantization parameters" on the same page: (M, B, g)
+ * are free hyperparameters, and e.g. (1, 4), (2, 8), ..., (8, 32) at B = 8
+ * all cost 2 bits per weight): 1 <= M <= AQLM_MAX_CODEBOOKS, 1 <= B <= 16,
+ * g in {1, 2, 4, 8, 16, 32}.  The two named there as XBit-MxB at g = 8,
+ * (1, 16, 8) "1x16" and (2, 8, 8) "2x8", run tuned kernels; every other
+ * triple runs general kernels with the same semantics.
  *
  * Memory layouts (all arrays contiguous, row-major, DEVICE pointers):
- *   codes      [out][in/g][M]  uint8 for B = 8; int16 for B = 16, where the
- *                              16-bit pattern read as unsigned is the index
+ *   codes      [out][in/g][M]  uint8 for B <= 8; 16-bit (int16) for
+ *                              9 <= B <= 16.  The codeword index is the low
+ *                              B bits of the stored pattern read as unsigned
+ *                              (the page notes that a B that is not a
+ *                              multiple of 8 leaves bits of its bytes unused)
  *   codebooks  [M][2^B][g]     fp16 (IEEE binary16, passed as opaque 16-bit
  *                              storage)
  *   scales     [out]           fp16
@@ -53,13 +59,15 @@ typedef enum {
     AQLM_OK = 0,
     AQLM_ERR_NULL = 1,   /* a required pointer is NULL (or decode got x != NULL) */
     AQLM_ERR_SHAPE = 2,  /* out/in/batch negative or out of range, in % g != 0 */
-    AQLM_ERR_SCHEME = 3, /* (M, B, g) not one of (1,16,8), (2,8,8) */
+    AQLM_ERR_SCHEME = 3, /* (M, B, g) outside 1..AQLM_MAX_CODEBOOKS x 1..16 x {1,2,4,8,16,32} */
     AQLM_ERR_ALIGN = 4,  /* codes, codebooks, x or y not 16-byte aligned, scales not 2-byte aligned */
     AQLM_ERR_HIP = 5     /* the HIP runtime reported an error at launch */
 } aqlm_status;
 
 /* Largest `in` accepted (inputs per row). */
 #define AQLM_MAX_IN (1 << 20)
+/* Most codebooks (M) a scheme may have. */
+#define AQLM_MAX_CODEBOOKS 8
 /* Largest batch of aqlm_linear_gemv. */
 #define AQLM_GEMV_MAX_BATCH 16
 

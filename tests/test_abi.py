@@ -72,8 +72,12 @@ def test_validation_product(lib, fn):
     assert call(fn, scales=0) == binding.AQLM_ERR_NULL
     assert call(fn, x=0) == binding.AQLM_ERR_NULL
     assert call(fn, y=0) == binding.AQLM_ERR_NULL
-    for M, B, g in ((3, 8, 8), (2, 16, 8), (1, 8, 8), (2, 8, 16), (1, 16, 4)):
+    for M, B, g in ((9, 8, 8), (0, 8, 8), (2, 17, 8), (1, 0, 8), (2, 8, 3), (1, 16, 64), (2, 8, 0)):
         assert call(fn, M=M, B=B, g=g) == binding.AQLM_ERR_SCHEME
+    # any 1 <= M <= 8, 1 <= B <= 16, g in {1, 2, 4, 8, 16, 32} is a scheme (nothing enqueued: out = 0)
+    for M, B, g in ((3, 8, 8), (2, 16, 8), (1, 8, 4), (8, 8, 32), (1, 16, 4), (1, 1, 1)):
+        assert call(fn, M=M, B=B, g=g, out=0, n_in=64) == binding.AQLM_OK
+    assert call(fn, M=1, B=8, g=32, n_in=48) == binding.AQLM_ERR_SHAPE   # in % g != 0
     assert call(fn, n_in=60) == binding.AQLM_ERR_SHAPE
     assert call(fn, n_in=0) == binding.AQLM_ERR_SHAPE
     assert call(fn, n_in=(1 << 20) + 8) == binding.AQLM_ERR_SHAPE
@@ -98,7 +102,7 @@ def test_validation_gemv_batch_limit(lib):
 def test_validation_decode(lib):
     assert call("aqlm_linear_decode", x=A) == binding.AQLM_ERR_NULL   # decode takes no x
     assert call("aqlm_linear_decode", x=0, y=0) == binding.AQLM_ERR_NULL
-    assert call("aqlm_linear_decode", x=0, M=1, B=8) == binding.AQLM_ERR_SCHEME
+    assert call("aqlm_linear_decode", x=0, M=1, B=17) == binding.AQLM_ERR_SCHEME
     assert call("aqlm_linear_decode", x=0, n_in=12) == binding.AQLM_ERR_SHAPE
     assert call("aqlm_linear_decode", x=0, out=1 << 30, n_in=1 << 10) == binding.AQLM_ERR_SHAPE
     assert call("aqlm_linear_decode", x=0, y=A + 8) == binding.AQLM_ERR_ALIGN
@@ -138,7 +142,7 @@ def test_validation_gemv_fused(lib):
     assert fused(l_out=[(1, -1)]) == binding.AQLM_ERR_SHAPE
     assert fused(x=0) == binding.AQLM_ERR_NULL
     assert fused(batch=17) == binding.AQLM_ERR_SHAPE
-    assert fused(M=1, B=8) == binding.AQLM_ERR_SCHEME
+    assert fused(M=1, B=17) == binding.AQLM_ERR_SCHEME
     # empty layers are skipped; an all-empty call enqueues nothing
     assert fused(out=0) == binding.AQLM_OK
     assert fused(out=0, l_codes=[(0, 0)]) == binding.AQLM_OK

@@ -325,6 +325,108 @@ def test_gemm_matches_gemv_for_small_batch():
 
 
 # --------------------------------------------------------------------------
+# Generic schemes: any (M, B, g), codes in whole bytes indexed by their low B bits
+
+GENERIC = [(1, 8, 4), (4, 8, 16), (8, 8, 32), (3, 5, 8), (1, 12, 4), (2, 16, 32), (1, 12, 1), (3, 5, 2),
+           (2, 8, 16), (1, 16, 8 // 2)]
+
+
+def junk_high_bits(codes, B, seed=7):
+    """Random bits in the unused high part of every stored code (the index is the low B bits)."""
+    rng = np.random.default_rng(seed)
+    bits = 8 if codes.dtype == np.uint8 else 16
+    if B == bits:
+        return codes.copy()
+    u = codes.view(np.uint8 if bits == 8 else np.uint16).astype(np.int64)
+    out = (u | (rng.integers(0, 1 << (bits - B), size=u.shape) << B)).astype(np.uint8 if bits == 8 else np.uint16)
+    return out if bits == 8 else out.view(np.int16)
+
+
+def gdev(L, codes):
+    return (torch.from_numpy(codes).cuda(), torch.from_numpy(L.codebooks).cuda(),
+            torch.from_numpy(L.scales).cuda(), torch.from_numpy(L.x).cuda())
+
+
+@pytest.mark.parametrize("M,B,g", GENERIC)
+def test_generic_decode_bit_exact(M, B, g):
+    L = synth.make_layer_mbg(M, B, g, 67, g * 37, seed=M + B + g)
+    codes = junk_high_bits(L.codes, B)
+    c, cb, s, _ = gdev(L, codes)
+    w = E.aqlm_linear_decode(c, cb, s)
+    torch.cuda.synchronize()
+    want = O.decode_fp16(codes, L.codebooks, L.scales)
+    np.testing.assert_array_equal(w.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,B,g", GENERIC)
+@pytest.mark.parametrize("batch", [1, 5, 16])
+def test_generic_gemv(M, B, g, batch):
+    L = synth.make_layer_mbg(M, B, g, 131, g * 45, batch=batch, seed=3 * M + B)
+    codes = junk_high_bits(L.codes, B)
+    c, cb, s, x = gdev(L, codes)
+    y = E.aqlm_linear_gemv(c, cb, s, x)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy().astype(np.float64), O.linear_ref_f64(codes, L.codebooks, L.scales, L.x),
+                 f"gemv {M}x{B}g{g} T{batch}")
+
+
+@pytest.mark.parametrize("M,B,g", GENERIC)
+@pytest.mark.parametrize("out,n_grp,batch", [(200, 37, 130), (64, 8, 3)])
+def test_generic_gemm(M, B, g, out, n_grp, batch):
+    """Several tiles with ragged rows, tokens and inputs (in % 8 != 0 when g < 8 and n_grp is odd)."""
+    L = synth.make_layer_mbg(M, B, g, out, g * n_grp, batch=batch, seed=5 * M + B + g)
+    codes = junk_high_bits(L.codes, B)
+    c, cb, s, x = gdev(L, codes)
+    y = E.aqlm_linear_gemm(c, cb, s, x)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy().astype(np.float64), O.linear_ref_f64(codes, L.codebooks, L.scales, L.x),
+                 f"gemm {M}x{B}g{g} {out}x{g * n_grp} T{batch}")
+
+
+@pytest.mark.parametrize("M,B,g", [(4, 8, 16), (1, 8, 4), (3, 5, 2)])
+def test_generic_exact_on_identity(M, B, g):
+    """Dyadic one-hot codebooks and X = I: GEMM and GEMV return W16 columns exactly."""
+    K = 1 << B
+    k = np.arange(K)
+    cb = np.zeros((M, K, g), np.float16)
+    for m in range(M):
+        cb[m, k, k % g] = (2.0 ** -(m + 1)) * ((k // g) % 32 + 1) / 32
+    n_in = 16 * g if g >= 8 else 64
+    L = synth.make_layer_mbg(M, B, g, 40, n_in, batch=n_in, seed=9)
+    L.codebooks = cb
+    L.scales = np.random.default_rng(2).choice([0.5, 1.0, 2.0], size=40).astype(np.float16)
+    L.x = np.eye(n_in, dtype=np.float16)
+    c, cbd, s, x = gdev(L, L.codes)
+    want = O.decode_fp16(L.codes, cb, L.scales).astype(np.float64).T
+    y = E.aqlm_linear_gemm(c, cbd, s, x)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), want)
+    y1 = E.aqlm_linear_gemv(c, cbd, s, x[:16].contiguous())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y1.cpu().numpy().astype(np.float64), want[:16])
+
+
+@pytest.mark.parametrize("M,B,g", [(4, 8, 16), (8, 8, 32), (1, 8, 4), (2, 12, 8)])
+def test_generic_full_size_7b(M, B, g):
+    """4096x4096 at 2 bits per weight: decode (sampled rows exact), GEMV b1, GEMM 2048 tokens."""
+    L = synth.make_layer_mbg(M, B, g, 4096, 4096, batch=1, seed=0)
+    c, cb, s, x = gdev(L, L.codes)
+    rows = sample_rows(4096, 40)
+    w = E.aqlm_linear_decode(c, cb, s)
+    y = E.aqlm_linear_gemv(c, cb, s, x)
+    xs = torch.from_numpy(synth.make_activations(4096, 2048, seed=1)).cuda()
+    yg = E.aqlm_linear_gemm(c, cb, s, xs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(w.cpu().numpy()[rows].view(np.uint16),
+                                  O.decode_fp16(L.codes, L.codebooks, L.scales, rows=rows).view(np.uint16))
+    assert_close(y.cpu().numpy().astype(np.float64)[:, rows],
+                 O.linear_ref_rows_f64(L.codes, L.codebooks, L.scales, L.x, rows), "gemv")
+    tok = np.array([0, 1, 255, 256, 1000, 2047])
+    assert_close(yg.cpu().numpy().astype(np.float64)[tok][:, rows],
+                 O.linear_ref_rows_f64(L.codes, L.codebooks, L.scales, xs.cpu().numpy()[tok], rows), "gemm")
+
+
+# --------------------------------------------------------------------------
 # Errors through the binding
 
 
@@ -332,7 +434,9 @@ def test_binding_errors_on_gpu():
     L = synth.make_layer("2x8", 64, 256, batch=1, seed=0)
     codes, cb, s, x = dev(L)
     with pytest.raises(ValueError):
-        E.aqlm_linear_gemv(codes, cb[:, :128].contiguous(), s, x)      # B = 7
+        E.aqlm_linear_gemv(codes, cb[:, :100].contiguous(), s, x)      # 100 codewords: not 2^B
+    with pytest.raises(ValueError):
+        E.aqlm_linear_gemv(codes, torch.zeros((2, 512, 8), dtype=torch.float16, device="cuda"), s, x)  # B = 9, uint8 codes
     with pytest.raises(ValueError):
         E.aqlm_linear_gemv(codes, cb, s, torch.zeros((17, 256), dtype=torch.float16, device="cuda"))
     with pytest.raises(ValueError):
