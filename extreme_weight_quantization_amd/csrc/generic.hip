@@ -13,12 +13,14 @@
 // every other triple:
 //   decode_generic_kernel : W16 exactly as the 1x16/2x8 decode kernel (fp32 sum
 //                           from codebook 0 upward, fp32 scale, one RNE rounding);
-//   gemv_generic_kernel   : batch 1..16, one wave per row, fp32 weights;
+//   gemv_generic_kernel   : batch 1..16, one wave per row, 16 waves per
+//                           workgroup, fp32 weights;
 //   gemm_generic_kernel   : any batch, 128x128 tiles, W decoded into LDS in
 //                           8-input chunks, 16x16x32 fp16 matrix-core products.
 // g is a template parameter so that a group's g weights stay in registers; M
 // and B are run-time values.  Codebooks of at most 64 KB are copied to LDS by
-// the GEMV and GEMM kernels, larger ones are read through L2.
+// the GEMM kernel and of at most 128 KB by the GEMV kernel (the 8x8 g=32 scheme's
+// 128 KB included); larger ones are read through L2.
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
@@ -28,8 +30,10 @@ namespace aqlm {
 
 namespace {
 
-constexpr size_t kGenericLdsCodebook = 65536;   // bytes of codebook staged in LDS at most
+constexpr size_t kGemvLdsCodebook = 131072;   // GEMV: bytes of codebook staged in LDS at most
+constexpr size_t kGemmLdsCodebook = 65536;    // GEMM (next to its 40 KB of tiles)
 constexpr int kGemvMaxBatchGeneric = 16;
+constexpr int kGemvGenericThreads = 1024;     // 16 waves, one row each
 
 // The codeword index of code i: the low B bits of its CB-byte stored pattern.
 template <int CB>
@@ -131,12 +135,12 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(const uint8_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// GEMV, batch 1..16: wave w of a workgroup takes rows 4*blockIdx + w, stepping by
-// 4*gridDim; lane l takes the row's groups l, l+64, ...  Weights stay fp32 (the
+// GEMV, batch 1..16: wave w of a workgroup takes rows 16*blockIdx + w, stepping by
+// 16*gridDim; lane l takes the row's groups l, l+64, ...  Weights stay fp32 (the
 // scale is applied once per output); each lane accumulates its groups' dot
 // products for every batch row, then the wave sums its lanes.
 template <int G, int CB, bool LDS>
-__global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(kGemvGenericThreads) void gemv_generic_kernel(const uint8_t* __restrict__ codes,
                                                            const f16* __restrict__ codebooks,
                                                            const f16* __restrict__ scales,
                                                            const f16* __restrict__ x, f16* __restrict__ y,
@@ -151,7 +155,8 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t* __rest
     const uint32_t mask = (1u << B) - 1u;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_grp = in / G;
-    for (int row = blockIdx.x * 4 + wave; row < out; row += gridDim.x * 4) {
+    constexpr int kRows = kGemvGenericThreads / 64;
+    for (int row = blockIdx.x * kRows + wave; row < out; row += gridDim.x * kRows) {
         float acc[kGemvMaxBatchGeneric];
 #pragma unroll
         for (int b = 0; b < kGemvMaxBatchGeneric; ++b) acc[b] = 0.f;
@@ -355,10 +360,10 @@ hipError_t gemv_g(const GenericScheme& sc, const void* codes, const void* codebo
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    const int64_t blocks_needed = (out + 3) / 4;
-    const int64_t cap = (int64_t)device_cu_count() * 8;
+    const int64_t blocks_needed = (out + 15) / 16;
+    const int64_t cap = (int64_t)device_cu_count() * (LDS ? 1 : 2);
     const int grid = (int)(blocks_needed < cap ? blocks_needed : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, (const uint8_t*)codes, (const f16*)codebooks,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemvGenericThreads), lds, stream, (const uint8_t*)codes, (const f16*)codebooks,
                        (const f16*)scales, (const f16*)x, (f16*)y, (int)out, (int)in, (int)batch, sc.M, sc.B);
     return hipGetLastError();
 }
@@ -402,7 +407,7 @@ hipError_t launch_decode_generic(const GenericScheme& sc, const void* codes, con
 hipError_t launch_gemv_generic(const GenericScheme& sc, const void* codes, const void* codebooks,
                                const void* scales, const void* x, void* y, int64_t out, int64_t in,
                                int64_t batch, hipStream_t stream) {
-    const bool lds = codebook_bytes(sc) <= kGenericLdsCodebook;
+    const bool lds = codebook_bytes(sc) <= kGemvLdsCodebook;
 #define AQLM_GV(G, CB) (lds ? gemv_g<G, CB, true>(sc, codes, codebooks, scales, x, y, out, in, batch, stream) \
                             : gemv_g<G, CB, false>(sc, codes, codebooks, scales, x, y, out, in, batch, stream))
     AQLM_DISPATCH_G(sc, AQLM_GV)
@@ -412,7 +417,7 @@ hipError_t launch_gemv_generic(const GenericScheme& sc, const void* codes, const
 hipError_t launch_gemm_generic(const GenericScheme& sc, const void* codes, const void* codebooks,
                                const void* scales, const void* x, void* y, int64_t out, int64_t in,
                                int64_t batch, hipStream_t stream) {
-    const bool lds = codebook_bytes(sc) <= kGenericLdsCodebook;
+    const bool lds = codebook_bytes(sc) <= kGemmLdsCodebook;
 #define AQLM_GM(G, CB) (lds ? gemm_g<G, CB, true>(sc, codes, codebooks, scales, x, y, out, in, batch, stream) \
                             : gemm_g<G, CB, false>(sc, codes, codebooks, scales, x, y, out, in, batch, stream))
     AQLM_DISPATCH_G(sc, AQLM_GM)
