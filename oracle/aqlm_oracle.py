@@ -211,3 +211,127 @@ MAX_ABS_FRAC = 1e-2
 def within_tolerance(y, y_ref):
     rel, mx, ref_max = parity_errors(y, y_ref)
     return rel <= REL_L2_TOL and mx <= MAX_ABS_FRAC * ref_max
+
+
+# ---------------------------------------------------------------------------
+# Encoding with fixed codebooks, and residual k-means codebook initialisation
+#
+# "The AQLM Quantization Algorithm, Explained", section "The AQLM quantization
+# procedure": per linear layer, the codes are learned first with the codebooks
+# fixed, and those codebooks are initialised with a residual k-means approach.
+# The learning loss itself did not survive text extraction and is weighted by
+# calibration activations, so these are the data-free readings, each listed in
+# DESIGN.md:
+#
+# * a group's target is its weights divided by the row's scale (scales are
+#   given; the pages do not say how they are initialised), in fp32;
+# * codes are chosen greedily, codebook 0 first: the code for codebook m is the
+#   nearest codeword (squared Euclidean distance) to what the earlier
+#   codebooks left over, and that codeword is subtracted;
+# * residual k-means runs Lloyd's algorithm on those leftovers for codebook 0,
+#   then on what codebook 0 leaves for codebook 1, and so on; its seeds are
+#   given groups (random numbers the method draws are inputs);
+# * distances are sum_t (r_t - c_t)^2 in fp32, t ascending, each operation
+#   rounded (no fused multiply-add); ties go to the lowest index;
+# * a centroid is the mean of its members, accumulated exactly in fixed point
+#   (each coordinate rounded to a multiple of 2^-24, summed as integers) and
+#   divided in float64, then rounded to fp32; an empty cluster keeps its
+#   centroid; the codebook is the fp16 rounding of the final centroids, and the
+#   codes are assigned against that fp16 codebook.
+
+KMEANS_FIXED_POINT = 2.0 ** 24
+
+
+def group_targets(w, scales, g):
+    """[out*in/g][g] fp32 group vectors: W[i][j*g+t] / s_i, one fp32 division each."""
+    w = np.asarray(w)
+    if w.dtype != np.float16 or scales.dtype != np.float16:
+        raise ValueError("w and scales must be float16")
+    out, n_in = w.shape
+    if n_in % g or scales.shape != (out,):
+        raise ValueError("w must be [out][in] with in % g == 0, scales [out]")
+    r = w.astype(np.float32) / scales.astype(np.float32)[:, None]
+    return r.reshape(out * (n_in // g), g)
+
+
+def nearest_codeword(r, cb32, chunk=1024):
+    """Index of the nearest row of cb32 [K][g] (fp32) for every row of r [N][g].
+
+    Distance sum_t (r_t - c_t)^2 in fp32, t ascending; the lowest index wins a tie.
+    """
+    N, g = r.shape
+    K = cb32.shape[0]
+    best = np.zeros(N, np.int64)
+    best_d = np.full(N, np.inf, np.float32)
+    for k0 in range(0, K, chunk):
+        c = cb32[k0:k0 + chunk]
+        d = np.zeros((N, c.shape[0]), np.float32)
+        for t in range(g):
+            e = r[:, None, t] - c[None, :, t]
+            d = d + e * e
+        kk = np.argmin(d, axis=1)
+        dd = d[np.arange(N), kk]
+        upd = dd < best_d
+        best[upd] = kk[upd] + k0
+        best_d[upd] = dd[upd]
+    return best
+
+
+def _store_codes(idx, B):
+    return idx.astype(np.uint8) if B <= 8 else idx.astype(np.uint16).view(np.int16)
+
+
+def encode_greedy(w, scales, codebooks):
+    """Codes [out][in/g][M] for W with fixed codebooks (greedy residual, m ascending)."""
+    M, K, g = codebooks.shape
+    B = K.bit_length() - 1
+    r = group_targets(w, scales, g).copy()
+    idx = np.zeros((r.shape[0], M), np.int64)
+    for m in range(M):
+        cb = codebooks[m].astype(np.float32)
+        idx[:, m] = nearest_codeword(r, cb)
+        r = r - cb[idx[:, m]]
+    out = w.shape[0]
+    return _store_codes(idx.reshape(out, -1, M), B)
+
+
+def kmeans_centroids(r, labels, prev):
+    """Lloyd update: per cluster, the fixed-point mean of its members (empty: previous centroid)."""
+    K, g = prev.shape
+    q = np.rint(r.astype(np.float64) * KMEANS_FIXED_POINT).astype(np.int64)
+    sums = np.zeros((K, g), np.int64)
+    np.add.at(sums, labels, q)
+    counts = np.bincount(labels, minlength=K).astype(np.int64)
+    c = prev.copy()
+    nz = counts > 0
+    c[nz] = (sums[nz].astype(np.float64) / KMEANS_FIXED_POINT / counts[nz, None].astype(np.float64)).astype(np.float32)
+    return c
+
+
+def kmeans_residual_init(w, scales, init_groups, M, B, g, iters):
+    """Residual k-means: (codebooks [M][2^B][g] fp16, codes [out][in/g][M]).
+
+    init_groups [M][2^B]: the group indices whose leftovers seed each codebook.
+    """
+    K = 1 << B
+    init_groups = np.asarray(init_groups, np.int64)
+    if init_groups.shape != (M, K):
+        raise ValueError("init_groups must be [M][2^B]")
+    r = group_targets(w, scales, g).copy()
+    codebooks = np.zeros((M, K, g), np.float16)
+    idx = np.zeros((r.shape[0], M), np.int64)
+    for m in range(M):
+        c = r[init_groups[m]].copy()
+        for _ in range(iters):
+            c = kmeans_centroids(r, nearest_codeword(r, c), c)
+        codebooks[m] = c.astype(np.float16)
+        cb = codebooks[m].astype(np.float32)
+        idx[:, m] = nearest_codeword(r, cb)
+        r = r - cb[idx[:, m]]
+    return codebooks, _store_codes(idx.reshape(w.shape[0], -1, M), B)
+
+
+def kmeans_objective(r, cb32, labels):
+    """Sum of squared distances of r to their centroids (float64)."""
+    d = r.astype(np.float64) - cb32.astype(np.float64)[labels]
+    return float((d * d).sum())

@@ -1,0 +1,183 @@
+"""Pins of the oracle's greedy encoder and residual k-means (CPU only).
+
+Each pin is checked against something other than the oracle's own formulas:
+planted codes and clusters whose answer is known by construction, brute force
+in float64, exact means, and the monotone objective of Lloyd's algorithm.
+"""
+import numpy as np
+import pytest
+
+from oracle import aqlm_oracle as O
+from extreme_weight_quantization_amd import synth
+
+
+def planted(M, B, g, out, n_in, seed, sigma=1.0):
+    """Codes and codebooks drawn at random, W16 = their decode (so W is exactly representable)."""
+    L = synth.make_layer_mbg(M, B, g, out, n_in, seed=seed, sigma=sigma)
+    return L, O.decode_fp16(L.codes, L.codebooks, L.scales)
+
+
+@pytest.mark.parametrize("B,g", [(8, 8), (4, 4), (12, 8), (6, 16)])
+def test_greedy_recovers_planted_codes_single_codebook(B, g):
+    """M = 1: W = s * C[b] rounded to fp16; the nearest codeword to W / s is C[b] itself."""
+    L, w = planted(1, B, g, 40, 8 * g, seed=B + g)
+    np.testing.assert_array_equal(O.encode_greedy(w, L.scales, L.codebooks), L.codes)
+
+
+def test_greedy_matches_float64_brute_force():
+    """M = 1 on random targets: the code is the float64 argmin of the Euclidean norm."""
+    rng = np.random.default_rng(3)
+    cb = rng.normal(0, 1, size=(1, 64, 4)).astype(np.float16)
+    w = rng.normal(0, 1, size=(30, 40)).astype(np.float16)
+    s = rng.uniform(0.5, 2.0, size=30).astype(np.float16)
+    codes = O.encode_greedy(w, s, cb)
+    r = w.astype(np.float64).reshape(30, 10, 4) / s.astype(np.float64)[:, None, None]
+    dist = np.linalg.norm(r[:, :, None, :] - cb[0].astype(np.float64)[None, None], axis=-1)
+    np.testing.assert_array_equal(codes[:, :, 0], np.argmin(dist, axis=-1))
+
+
+def test_greedy_ties_take_the_lowest_index():
+    """Duplicated codewords: the later copy is never chosen."""
+    rng = np.random.default_rng(4)
+    base = rng.normal(0, 1, size=(16, 8)).astype(np.float16)
+    cb = np.concatenate([base, base])[None]              # codeword k and k+16 are equal
+    w = rng.normal(0, 1, size=(8, 64)).astype(np.float16)
+    codes = O.encode_greedy(w, np.ones(8, np.float16), cb)
+    assert codes.max() < 16
+
+
+def test_greedy_subtracts_each_chosen_codeword():
+    """Nested codebooks {0, v} and {0, v}: a group equal to v encodes as (1, 0), 2v as (1, 1).
+
+    Without the subtraction of codebook 0's choice the second code of the group
+    v would also be 1 and the decode would give 2v.
+    """
+    v = np.array([1, -2, 0.5, 3, 0, 1, -1, 2], np.float16)
+    cb = np.zeros((2, 2, 8), np.float16)
+    cb[0, 1] = v
+    cb[1, 1] = v
+    w = np.stack([np.concatenate([v, 2 * v, 0 * v])]).astype(np.float16)
+    codes = O.encode_greedy(w, np.ones(1, np.float16), cb)
+    assert codes[0].tolist() == [[1, 0], [1, 1], [0, 0]]
+    np.testing.assert_array_equal(O.decode_fp16(codes, cb, np.ones(1, np.float16)), w)
+
+
+def test_greedy_each_step_is_the_nearest_to_the_leftover():
+    """M = 3: codebook m's code is the float64 nearest codeword to W/s minus the earlier choices."""
+    rng = np.random.default_rng(5)
+    cb = rng.normal(0, 0.5, size=(3, 32, 8)).astype(np.float16)
+    w = rng.normal(0, 1, size=(12, 32)).astype(np.float16)
+    s = np.ones(12, np.float16)
+    codes = O.encode_greedy(w, s, cb).reshape(-1, 3).astype(np.int64)
+    r = w.astype(np.float64).reshape(-1, 8)
+    for m in range(3):
+        dist = np.linalg.norm(r[:, None, :] - cb[m].astype(np.float64)[None], axis=-1)
+        np.testing.assert_array_equal(codes[:, m], np.argmin(dist, axis=1))
+        r = r - cb[m].astype(np.float64)[codes[:, m]]
+
+
+def test_greedy_codes_use_the_scheme_storage():
+    L, w = planted(1, 12, 4, 6, 16, seed=1)
+    c = O.encode_greedy(w, L.scales, L.codebooks)
+    assert c.dtype == np.int16 and c.shape == (6, 4, 1)
+    L, w = planted(2, 5, 4, 6, 16, seed=1)
+    assert O.encode_greedy(w, L.scales, L.codebooks).dtype == np.uint8
+
+
+def clustered_weights(K, g, per, seed, spread=1e-3):
+    """K well-separated centres, `per` noisy copies of each, shuffled into a [rows][g*cols] matrix."""
+    rng = np.random.default_rng(seed)
+    centres = rng.normal(0, 1, size=(K, g)) * 4
+    labels = np.repeat(np.arange(K), per)
+    pts = centres[labels] + rng.normal(0, spread, size=(K * per, g))
+    perm = rng.permutation(K * per)
+    pts, labels = pts[perm], labels[perm]
+    cols = 4
+    w = pts.reshape(-1, cols * g).astype(np.float16)
+    return w, labels, pts
+
+
+def test_kmeans_separated_clusters_reach_the_exact_means():
+    """One seed per planted cluster: Lloyd's algorithm labels every point with its cluster and
+    every centroid equals the float64 mean of its points (fixed-point accumulation: within
+    2^-25 per coordinate before the fp32 and fp16 roundings)."""
+    K, g = 16, 8
+    w, labels, _ = clustered_weights(K, g, per=24, seed=6)
+    s = np.ones(w.shape[0], np.float16)
+    r = O.group_targets(w, s, g)
+    seeds = np.array([np.flatnonzero(labels == k)[0] for k in range(K)])
+    c = r[seeds].copy()
+    for _ in range(3):
+        lab = O.nearest_codeword(r, c)
+        c = O.kmeans_centroids(r, lab, c)
+    np.testing.assert_array_equal(O.nearest_codeword(r, c), labels)
+    exact = np.stack([r[labels == k].astype(np.float64).mean(0) for k in range(K)])
+    assert np.max(np.abs(c.astype(np.float64) - exact)) <= 2.0 ** -25 + np.max(np.abs(exact)) * 2.0 ** -23
+
+
+def test_kmeans_objective_never_increases():
+    """Lloyd's algorithm: each assign + update step does not raise the sum of squared distances."""
+    rng = np.random.default_rng(7)
+    r = rng.normal(0, 1, size=(600, 4)).astype(np.float32)
+    c = r[rng.choice(600, 32, replace=False)].copy()
+    prev = np.inf
+    for _ in range(6):
+        lab = O.nearest_codeword(r, c)
+        obj = O.kmeans_objective(r, c, lab)
+        assert obj <= prev * (1 + 1e-9)
+        prev = obj
+        c = O.kmeans_centroids(r, lab, c)
+
+
+def test_kmeans_every_point_its_own_cluster():
+    """K = N distinct points, each seeding one cluster: centroids are the points (to 2^-25), codes the seed order."""
+    rng = np.random.default_rng(8)
+    r = rng.normal(0, 1, size=(16, 4)).astype(np.float32)
+    perm = rng.permutation(16)
+    c = r[perm].copy()
+    lab = O.nearest_codeword(r, c)
+    np.testing.assert_array_equal(perm[lab], np.arange(16))
+    c2 = O.kmeans_centroids(r, lab, c)
+    assert np.max(np.abs(c2 - c)) <= 2.0 ** -25
+
+
+def test_kmeans_empty_cluster_keeps_its_centroid():
+    r = np.array([[0, 0], [0.1, 0], [5, 5]], np.float32)
+    prev = np.array([[0, 0], [100, 100], [5, 5]], np.float32)
+    c = O.kmeans_centroids(r, O.nearest_codeword(r, prev), prev)
+    np.testing.assert_array_equal(c[1], prev[1])
+
+
+def test_residual_kmeans_seeds_and_chaining():
+    """iters = 0: codebook 0 is the fp16 targets at its seeds; codebook 1 is the fp16 leftovers of
+    those targets after codebook 0's greedy choice, at its own seeds."""
+    rng = np.random.default_rng(9)
+    M, B, g = 2, 3, 4
+    w = rng.normal(0, 1, size=(6, 16)).astype(np.float16)
+    s = rng.uniform(0.5, 1.5, size=6).astype(np.float16)
+    seeds = np.stack([rng.choice(24, 8, replace=False) for _ in range(M)])
+    cb, codes = O.kmeans_residual_init(w, s, seeds, M, B, g, iters=0)
+    r = w.astype(np.float32).reshape(6, 4, g) / s.astype(np.float32)[:, None, None]
+    r = r.reshape(24, g)
+    np.testing.assert_array_equal(cb[0], r[seeds[0]].astype(np.float16))
+    left = r - cb[0].astype(np.float32)[codes.reshape(24, M)[:, 0].astype(np.int64)]
+    np.testing.assert_array_equal(cb[1], left[seeds[1]].astype(np.float16))
+    # and the codes are the greedy encoding against the final codebooks
+    np.testing.assert_array_equal(codes, O.encode_greedy(w, s, cb))
+
+
+def test_residual_kmeans_on_planted_clusters_recovers_the_layer():
+    """W made of 8 distinct codewords of one codebook (each repeated), seeded one per codeword and
+    padded by duplicates: k-means finds the codewords and the decode equals W."""
+    rng = np.random.default_rng(10)
+    K, g = 8, 8
+    words = (rng.normal(0, 1, size=(K, g)) * 3).astype(np.float16)
+    lab = rng.integers(0, K, size=64)
+    lab[:K] = np.arange(K)
+    w = words[lab].reshape(16, 4 * g)
+    s = np.ones(16, np.float16)
+    B = 4   # 16 codewords: seeds 0..7 are the distinct ones, the rest repeat seed 0
+    seeds = np.concatenate([np.arange(K), np.zeros(16 - K, np.int64)])[None]
+    cb, codes = O.kmeans_residual_init(w, s, seeds, 1, B, g, iters=2)
+    np.testing.assert_array_equal(O.decode_fp16(codes, cb, s), w)
+    assert codes.max() < K   # duplicates of seed 0 tie with it and lose

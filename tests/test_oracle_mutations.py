@@ -41,9 +41,25 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_mutant(name, tmp_path):
-    before, after = MUTANTS[name]
+# Mistakes in the encoder and residual k-means, caught by test_oracle_encode.py.
+ENCODE_MUTANTS = {
+    "greedy_no_subtract": ("        r = r - cb[idx[:, m]]\n    out = w.shape[0]", "    out = w.shape[0]"),
+    "ties_take_last": ("kk = np.argmin(d, axis=1)", "kk = d.shape[1] - 1 - np.argmin(d[:, ::-1], axis=1)"),
+    "distance_abs": ("d = d + e * e", "d = d + np.abs(e)"),
+    "centroid_is_a_sum": (
+        " / KMEANS_FIXED_POINT / counts[nz, None].astype(np.float64)).astype(np.float32)",
+        " / KMEANS_FIXED_POINT).astype(np.float32)"),
+    "kmeans_residual_not_chained": ("        r = r - cb[idx[:, m]]\n    return codebooks", "    return codebooks"),
+    "targets_times_scale": ("r = w.astype(np.float32) / scales.astype(np.float32)[:, None]",
+                            "r = w.astype(np.float32) * scales.astype(np.float32)[:, None]"),
+}
+CASES = [(n, MUTANTS[n], "test_oracle.py") for n in sorted(MUTANTS)] + \
+        [(n, ENCODE_MUTANTS[n], "test_oracle_encode.py") for n in sorted(ENCODE_MUTANTS)]
+
+
+@pytest.mark.parametrize("name,mutant,pins", CASES, ids=[c[0] for c in CASES])
+def test_pins_catch_mutant(name, mutant, pins, tmp_path):
+    before, after = mutant
     src = open(os.path.join(ROOT, "oracle", "aqlm_oracle.py")).read()
     assert before in src, f"mutation site for {name} not found"
     dst = tmp_path / "oracle"
@@ -51,6 +67,6 @@ def test_pins_catch_mutant(name, tmp_path):
     (dst / "aqlm_oracle.py").write_text(src.replace(before, after))
     env = dict(os.environ, AQLM_ORACLE_MUTANT_DIR=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        capture_output=True, text=True, env=env, cwd=ROOT, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived:\n{r.stdout[-2000:]}"
