@@ -29,7 +29,10 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
+MFMA_F16_PEAK_TFLOPS = 2500
+# fp32 vector ALU: 157.3 TFLOP/s counts a fused multiply-add as 2 flops, so a
+# plain (unfused) add, subtract or multiply peaks at half that op rate.
+VALU_F32_PEAK_TOPS = 157.3 / 2.0  # MI355X dense fp16 matrix cores
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 
 BLOCK_7B = ((4096, 4096),) * 4 + ((11008, 4096),) * 2 + ((4096, 11008),)
@@ -426,6 +429,31 @@ def main():
             del cbg, codes, s, w, x1, y1, x2, y2
             torch.cuda.empty_cache()
         breakdown["generic_schemes"] = gs
+        # greedy residual encoder and residual k-means (3 unfused fp32 ops per codeword entry compared)
+        en = {}
+        for (M, B, g, out, n_in, iters) in ((2, 8, 8, 4096, 4096, 0), (2, 8, 8, 4096, 4096, 10),
+                                            (1, 16, 8, 1024, 4096, 0)):
+            w = (torch.randn((out, n_in), generator=gen, device="cuda") * 0.05).half()
+            s = ((torch.rand(out, generator=gen, device="cuda") + 0.5) * 0.05).half()
+            cbg = torch.randn((M, 1 << B, g), generator=gen, device="cuda").half()
+            n_grp = out * n_in // g
+            if iters == 0:
+                us = time_calls(torch, lambda i: E.aqlm_encode_greedy(w, s, cbg), 3, 1)
+                ops = 3.0 * n_grp * (1 << B) * g * M
+                en[f"greedy_{M}x{B}g{g}_{out}x{n_in}"] = {
+                    "us": round(us, 1), "Tops": round(ops / (us * 1e-6) / 1e12, 2),
+                    "frac_valu_peak": round(ops / (us * 1e-6) / 1e12 / VALU_F32_PEAK_TOPS, 4)}
+            else:
+                seeds = torch.randint(0, n_grp, (M, 1 << B), generator=gen, device="cuda", dtype=torch.int64)
+                ws = torch.empty(E.kmeans_workspace_bytes(M, B, g), dtype=torch.uint8, device="cuda")
+                us = time_calls(torch, lambda i: E.aqlm_kmeans_init(w, s, seeds, B, g, iters, workspace=ws), 2, 1)
+                ops = 3.0 * n_grp * (1 << B) * g * M * (iters + 1)
+                en[f"kmeans_{M}x{B}g{g}_{out}x{n_in}_iters{iters}"] = {
+                    "us": round(us, 1), "Tops": round(ops / (us * 1e-6) / 1e12, 2),
+                    "frac_valu_peak": round(ops / (us * 1e-6) / 1e12 / VALU_F32_PEAK_TOPS, 4)}
+            del w, s, cbg
+            torch.cuda.empty_cache()
+        breakdown["encode"] = en
         # fp16 comparator (torch.matmul on dense fp16 weights: the vendor BLAS), the
         # denominator of the "speedup vs FP16" figures the AQLM pages quote.
         cmp16 = {}

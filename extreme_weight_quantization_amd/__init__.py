@@ -11,6 +11,9 @@ from .binding import (  # noqa: F401
     aqlm_linear_gemm,
     aqlm_linear_gemv,
     aqlm_linear_gemv_fused,
+    aqlm_encode_greedy,
+    aqlm_kmeans_init,
+    kmeans_workspace_bytes,
     load_library,
     status_str,
 )

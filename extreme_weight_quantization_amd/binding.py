@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaqlm.so"
 
 AQLM_OK, AQLM_ERR_NULL, AQLM_ERR_SHAPE, AQLM_ERR_SCHEME, AQLM_ERR_ALIGN, AQLM_ERR_HIP = range(6)
 EXPORTED = ("aqlm_linear_gemv", "aqlm_linear_gemv_fused", "aqlm_linear_gemm", "aqlm_linear_decode",
+            "aqlm_encode_greedy", "aqlm_kmeans_workspace_bytes", "aqlm_kmeans_init",
             "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
 FUSED_MAX_LAYERS = 8   # AQLM_FUSED_MAX_LAYERS
 
@@ -49,6 +50,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.aqlm_linear_gemv_fused.argtypes = [ci, pp, pp, pp, ctypes.POINTER(i64), vp, pp,
                                                ci, ci, ci, i64, i64, vp]
         lib.aqlm_linear_gemv_fused.restype = ci
+        lib.aqlm_encode_greedy.argtypes = [vp, vp, vp, vp, ci, ci, ci, i64, i64, vp]
+        lib.aqlm_encode_greedy.restype = ci
+        lib.aqlm_kmeans_workspace_bytes.argtypes = [ci, ci, ci, ctypes.POINTER(i64)]
+        lib.aqlm_kmeans_workspace_bytes.restype = ci
+        lib.aqlm_kmeans_init.argtypes = [vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, i64, i64, ci, vp]
+        lib.aqlm_kmeans_init.restype = ci
         lib.aqlm_status_str.argtypes = [ci]
         lib.aqlm_status_str.restype = ctypes.c_char_p
         lib.aqlm_last_hip_error.argtypes = []
@@ -198,6 +205,72 @@ def aqlm_linear_decode(codes, codebooks, scales, w=None):
     _check(load_library().aqlm_linear_decode(_ptr(codes), _ptr(codebooks), _ptr(scales), None,
                                              _ptr(w), M, B, g, out, G * g, 0, _stream(codes.device)))
     return w
+
+
+def _check_weights(w, scales, g):
+    for name, t in (("w", w), ("scales", scales)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float16:
+            raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
+    if w.dim() != 2 or scales.shape != (w.shape[0],):
+        raise ValueError("w must be [out][in] and scales [out]")
+    if w.shape[1] % g:
+        raise ValueError("in must be a multiple of g")
+
+
+def _codes_out(codes, out, G, M, B, device):
+    dtype = torch.uint8 if B <= 8 else torch.int16
+    if codes is None:
+        return torch.empty((out, G, M), dtype=dtype, device=device)
+    if codes.shape != (out, G, M) or codes.dtype != dtype or not codes.is_contiguous():
+        raise ValueError(f"codes must be a contiguous {dtype} [{out}][{G}][{M}] tensor")
+    return codes
+
+
+def aqlm_encode_greedy(w, scales, codebooks, codes=None):
+    """Greedy residual codes [out][in/g][M] of w with fixed codebooks (see aqlm.h)."""
+    if codebooks.dim() != 3 or codebooks.dtype != torch.float16 or not codebooks.is_cuda:
+        raise ValueError("codebooks must be a float16 GPU tensor [M][2^B][g]")
+    M, K, g = (int(v) for v in codebooks.shape)
+    B = K.bit_length() - 1
+    if K != 1 << B:
+        raise ValueError("the codebook size must be a power of two")
+    _check_weights(w, scales, g)
+    out, n_in = int(w.shape[0]), int(w.shape[1])
+    codes = _codes_out(codes, out, n_in // g, M, B, w.device)
+    _check(load_library().aqlm_encode_greedy(_ptr(w), _ptr(scales), _ptr(codebooks.contiguous()), _ptr(codes),
+                                             M, B, g, out, n_in, _stream(w.device)))
+    return codes
+
+
+def kmeans_workspace_bytes(M, B, g) -> int:
+    n = ctypes.c_int64(0)
+    _check(load_library().aqlm_kmeans_workspace_bytes(M, B, g, ctypes.byref(n)))
+    return int(n.value)
+
+
+def aqlm_kmeans_init(w, scales, seeds, B, g, iters, codebooks=None, codes=None, workspace=None):
+    """Residual k-means codebooks [M][2^B][g] and their greedy codes (see aqlm.h).
+
+    seeds: int64 GPU tensor [M][2^B] of group indices (row * in/g + j)."""
+    if seeds.dim() != 2 or seeds.dtype != torch.int64 or not seeds.is_cuda or not seeds.is_contiguous():
+        raise ValueError("seeds must be a contiguous int64 GPU tensor [M][2^B]")
+    M = int(seeds.shape[0])
+    if int(seeds.shape[1]) != 1 << B:
+        raise ValueError("seeds must have 2^B columns")
+    _check_weights(w, scales, g)
+    out, n_in = int(w.shape[0]), int(w.shape[1])
+    if codebooks is None:
+        codebooks = torch.empty((M, 1 << B, g), dtype=torch.float16, device=w.device)
+    elif codebooks.shape != (M, 1 << B, g) or codebooks.dtype != torch.float16 or not codebooks.is_contiguous():
+        raise ValueError("codebooks must be a contiguous float16 [M][2^B][g] tensor")
+    codes = _codes_out(codes, out, n_in // g, M, B, w.device)
+    need = kmeans_workspace_bytes(M, B, g)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
+    _check(load_library().aqlm_kmeans_init(_ptr(w), _ptr(scales), _ptr(seeds), _ptr(codebooks), _ptr(codes),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           M, B, g, out, n_in, int(iters), _stream(w.device)))
+    return codebooks, codes
 
 
 def raw_call_fused(n_layers, codes, codebooks, scales, outs, x, ys, M, B, g, n_in, batch, stream=0) -> int:

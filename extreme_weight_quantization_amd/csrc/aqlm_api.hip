@@ -160,6 +160,48 @@ int aqlm_linear_decode(const void* codes, const void* codebooks, const void* sca
     return finish(launch_decode(scheme, codes, codebooks, scales, y, out, in, (hipStream_t)stream));
 }
 
+// Shared checks of the encoder entry points (scheme, shape, pointers, alignment).
+static int validate_encode(const void* w, const void* scales, const void* codebooks, const void* codes, int M, int B,
+                           int g, int64_t out, int64_t in, bool* empty) {
+    if (!generic_scheme_ok(M, B, g)) return AQLM_ERR_SCHEME;
+    if (out < 0 || out > (int64_t)INT32_MAX || in < 1 || in > AQLM_MAX_IN || (in % g) != 0) return AQLM_ERR_SHAPE;
+    *empty = out == 0;
+    if (*empty) return AQLM_OK;
+    if (!w || !scales || !codebooks || !codes) return AQLM_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(codebooks, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return AQLM_ERR_ALIGN;
+    return AQLM_OK;
+}
+
+int aqlm_encode_greedy(const void* w, const void* scales, const void* codebooks, void* codes, int M, int B, int g,
+                       int64_t out, int64_t in, void* stream) {
+    bool empty = false;
+    const int st = validate_encode(w, scales, codebooks, codes, M, B, g, out, in, &empty);
+    if (st != AQLM_OK || empty) return st;
+    return finish(launch_encode_greedy(w, scales, codebooks, codes, M, B, g, out, in, (hipStream_t)stream));
+}
+
+int aqlm_kmeans_workspace_bytes(int M, int B, int g, int64_t* bytes) {
+    if (!bytes) return AQLM_ERR_NULL;
+    if (!generic_scheme_ok(M, B, g)) return AQLM_ERR_SCHEME;
+    *bytes = kmeans_workspace_bytes(M, B, g);
+    return AQLM_OK;
+}
+
+int aqlm_kmeans_init(const void* w, const void* scales, const int64_t* seeds, void* codebooks, void* codes,
+                     void* workspace, int64_t workspace_bytes, int M, int B, int g, int64_t out, int64_t in,
+                     int iters, void* stream) {
+    bool empty = false;
+    int st = validate_encode(w, scales, codebooks, codes, M, B, g, out, in, &empty);
+    if (st != AQLM_OK) return st;
+    if (iters < 0 || iters > AQLM_KMEANS_MAX_ITERS) return AQLM_ERR_SHAPE;
+    if (empty) return AQLM_OK;
+    if (!seeds || !workspace) return AQLM_ERR_NULL;
+    if (!aligned(seeds, 8) || !aligned(workspace, 16)) return AQLM_ERR_ALIGN;
+    if (workspace_bytes < kmeans_workspace_bytes(M, B, g)) return AQLM_ERR_SHAPE;
+    return finish(launch_kmeans_init(w, scales, seeds, codebooks, codes, workspace, M, B, g, out, in, iters,
+                                     (hipStream_t)stream));
+}
+
 const char* aqlm_status_str(int status) {
     switch (status) {
         case AQLM_OK: return "AQLM_OK";

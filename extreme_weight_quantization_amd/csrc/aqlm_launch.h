@@ -19,6 +19,14 @@ hipError_t launch_decode_generic(const GenericScheme& sc, const void* codes, con
 hipError_t launch_gemv_generic(const GenericScheme& sc, const void* codes, const void* codebooks,
                                const void* scales, const void* x, void* y, int64_t out, int64_t in,
                                int64_t batch, hipStream_t stream);
+// Greedy residual codes with fixed codebooks, and residual k-means (encode.hip).
+hipError_t launch_encode_greedy(const void* w, const void* scales, const void* codebooks, void* codes, int M, int B,
+                                int g, int64_t out, int64_t in, hipStream_t stream);
+hipError_t launch_kmeans_init(const void* w, const void* scales, const int64_t* seeds, void* codebooks, void* codes,
+                              void* workspace, int M, int B, int g, int64_t out, int64_t in, int iters,
+                              hipStream_t stream);
+int64_t kmeans_workspace_bytes(int M, int B, int g);
+
 hipError_t launch_gemm_generic(const GenericScheme& sc, const void* codes, const void* codebooks,
                                const void* scales, const void* x, void* y, int64_t out, int64_t in,
                                int64_t batch, hipStream_t stream);

@@ -126,6 +126,53 @@ int aqlm_linear_decode(const void* codes, const void* codebooks, const void* sca
                        const void* x, void* y, int M, int B, int g,
                        int64_t out, int64_t in, int64_t batch, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Building the representation ("The AQLM quantization procedure" on the same
+ * page: per layer, the codes are learned first with fixed codebooks that a
+ * residual k-means initialises).  The page's learning loss is lost and needs
+ * calibration data; these are its data-free counterparts on plain weights:
+ *
+ *   target of a group    W[i][j*g .. j*g+g) / s_i, one fp32 division each;
+ *   code of codebook m   the nearest codeword (squared Euclidean distance,
+ *                        sum_t (r_t - c_t)^2 in fp32, t ascending, no fused
+ *                        multiply-add, lowest index on a tie) to the target
+ *                        minus the codewords chosen for codebooks 0 .. m-1.
+ *
+ * w is [out][in] fp16 (16-byte aligned), scales [out] fp16 (the page does not
+ * say how scales are initialised; the caller gives them), codes and
+ * codebooks as above.  Both calls accept every scheme the products accept.
+ * out == 0 enqueues nothing.  Results are deterministic and bit-identical to
+ * the plain CPU definition.
+ */
+
+/* Greedy residual codes for w with the given codebooks; writes codes. */
+int aqlm_encode_greedy(const void* w, const void* scales, const void* codebooks, void* codes,
+                       int M, int B, int g, int64_t out, int64_t in, void* stream);
+
+/* Largest iteration count aqlm_kmeans_init accepts. */
+#define AQLM_KMEANS_MAX_ITERS 10000
+
+/* Bytes of device workspace aqlm_kmeans_init needs for the scheme (into *bytes). */
+int aqlm_kmeans_workspace_bytes(int M, int B, int g, int64_t* bytes);
+
+/*
+ * Residual k-means: for m = 0 .. M-1, Lloyd's algorithm (`iters` rounds of
+ * assign + update) on what codebooks 0 .. m-1 leave of every group's target,
+ * seeded with the leftovers of groups seeds[m][0 .. 2^B-1] (device int64
+ * [M][2^B], group index = row * in/g + j, clamped into range); writes the fp16
+ * codebooks [M][2^B][g] and the codes of the greedy encoding against them.
+ * A centroid is the mean of its members, summed exactly as integers in units
+ * of 2^-24 and divided in float64, then rounded to fp32; an empty cluster
+ * keeps its centroid; codebook m is the fp16 rounding of the centroids.  The
+ * sums stay exact while a cluster's coordinate sum is below 2^29 in
+ * magnitude (e.g. |W/s| < 256 with up to 2^21 groups).  `workspace` is
+ * caller-owned device memory of at least aqlm_kmeans_workspace_bytes bytes
+ * (16-byte aligned); its contents on entry do not matter.
+ */
+int aqlm_kmeans_init(const void* w, const void* scales, const int64_t* seeds, void* codebooks, void* codes,
+                     void* workspace, int64_t workspace_bytes, int M, int B, int g,
+                     int64_t out, int64_t in, int iters, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* aqlm_status_str(int status);
 

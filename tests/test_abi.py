@@ -149,6 +149,62 @@ def test_validation_gemv_fused(lib):
     assert fused(batch=0) == binding.AQLM_OK
 
 
+def enc(**kw):
+    a = dict(w=A, scales=A, codebooks=A, codes=A, M=2, B=8, g=8, out=16, n_in=64)
+    a.update(kw)
+    return int(lib_fn("aqlm_encode_greedy")(a["w"], a["scales"], a["codebooks"], a["codes"], a["M"], a["B"], a["g"],
+                                            a["out"], a["n_in"], None))
+
+
+def km(**kw):
+    a = dict(w=A, scales=A, seeds=A, codebooks=A, codes=A, ws=A, ws_bytes=1 << 30, M=2, B=8, g=8, out=16, n_in=64,
+             iters=3)
+    a.update(kw)
+    return int(lib_fn("aqlm_kmeans_init")(a["w"], a["scales"], a["seeds"], a["codebooks"], a["codes"], a["ws"],
+                                          a["ws_bytes"], a["M"], a["B"], a["g"], a["out"], a["n_in"], a["iters"], None))
+
+
+def lib_fn(name):
+    return getattr(E.load_library(), name)
+
+
+def test_kmeans_workspace_bytes(lib):
+    import ctypes as C
+    n = C.c_int64(0)
+    assert lib.aqlm_kmeans_workspace_bytes(2, 8, 8, C.byref(n)) == binding.AQLM_OK
+    assert n.value == 256 * 8 * 8 + 256 * 8 + 256 * 8 * 4       # int64 sums, int64 counts, fp32 centroids
+    assert lib.aqlm_kmeans_workspace_bytes(1, 16, 8, C.byref(n)) == binding.AQLM_OK
+    assert n.value == 65536 * (8 * 12 + 8)
+    assert lib.aqlm_kmeans_workspace_bytes(2, 17, 8, C.byref(n)) == binding.AQLM_ERR_SCHEME
+    assert lib.aqlm_kmeans_workspace_bytes(2, 8, 8, None) == binding.AQLM_ERR_NULL
+    assert binding.kmeans_workspace_bytes(4, 8, 16) == 256 * (16 * 12 + 8)
+
+
+def test_validation_encode(lib):
+    for key in ("w", "scales", "codebooks", "codes"):
+        assert enc(**{key: 0}) == binding.AQLM_ERR_NULL
+    assert enc(M=9) == binding.AQLM_ERR_SCHEME
+    assert enc(g=3) == binding.AQLM_ERR_SCHEME
+    assert enc(n_in=60) == binding.AQLM_ERR_SHAPE
+    assert enc(out=-1) == binding.AQLM_ERR_SHAPE
+    assert enc(w=A + 8) == binding.AQLM_ERR_ALIGN
+    assert enc(codes=A + 2) == binding.AQLM_ERR_ALIGN
+    assert enc(scales=A + 1) == binding.AQLM_ERR_ALIGN
+    assert enc(out=0, w=0) == binding.AQLM_OK
+
+
+def test_validation_kmeans(lib):
+    for key in ("w", "scales", "codebooks", "codes", "seeds", "ws"):
+        assert km(**{key: 0}) == binding.AQLM_ERR_NULL
+    assert km(B=0) == binding.AQLM_ERR_SCHEME
+    assert km(iters=-1) == binding.AQLM_ERR_SHAPE
+    assert km(iters=10001) == binding.AQLM_ERR_SHAPE
+    assert km(ws_bytes=256 * (8 * 12 + 8) - 1) == binding.AQLM_ERR_SHAPE
+    assert km(seeds=A + 4) == binding.AQLM_ERR_ALIGN
+    assert km(ws=A + 8) == binding.AQLM_ERR_ALIGN
+    assert km(out=0, seeds=0, ws=0) == binding.AQLM_OK
+
+
 def test_binding_rejects_cpu_tensors(lib):
     import torch
     codes = torch.zeros((4, 8, 2), dtype=torch.uint8)

@@ -427,6 +427,79 @@ def test_generic_full_size_7b(M, B, g):
 
 
 # --------------------------------------------------------------------------
+# Greedy residual encoder and residual k-means (bit-exact against the oracle)
+
+
+def weights(out, n_in, seed, sigma=0.05):
+    rng = np.random.default_rng(seed)
+    w = rng.normal(0, sigma, size=(out, n_in)).astype(np.float16)
+    s = rng.uniform(0.5, 1.5, size=out).astype(np.float16) * np.float16(sigma)
+    return w, s.astype(np.float16)
+
+
+ENC_SCHEMES = [(2, 8, 8), (1, 16, 8), (4, 8, 16), (1, 12, 4), (3, 5, 2), (8, 8, 32)]
+
+
+@pytest.mark.parametrize("M,B,g", ENC_SCHEMES)
+def test_encode_greedy_bit_exact(M, B, g):
+    out, n_in = (24, 4 * g) if B > 12 else (67, 6 * g)
+    w, s = weights(out, n_in, seed=M + B)
+    cb = np.random.default_rng(1).normal(0, 1, size=(M, 1 << B, g)).astype(np.float16)
+    codes = E.aqlm_encode_greedy(torch.from_numpy(w).cuda(), torch.from_numpy(s).cuda(), torch.from_numpy(cb).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(codes.cpu().numpy(), O.encode_greedy(w, s, cb))
+
+
+def test_encode_greedy_recovers_planted_codes():
+    L = synth.make_layer_mbg(1, 8, 8, 300, 512, seed=4, sigma=1.0)
+    w = O.decode_fp16(L.codes, L.codebooks, L.scales)
+    codes = E.aqlm_encode_greedy(torch.from_numpy(w).cuda(), torch.from_numpy(L.scales).cuda(),
+                                 torch.from_numpy(L.codebooks).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(codes.cpu().numpy(), L.codes)
+
+
+@pytest.mark.parametrize("M,B,g,out,n_in,iters", [
+    (2, 8, 8, 64, 256, 3),
+    (1, 8, 4, 40, 64, 4),
+    (3, 5, 8, 33, 96, 2),
+    (1, 12, 4, 64, 64, 2),
+])
+def test_kmeans_init_bit_exact(M, B, g, out, n_in, iters):
+    w, s = weights(out, n_in, seed=out)
+    N = out * n_in // g
+    rng = np.random.default_rng(2)
+    seeds = np.stack([rng.choice(N, 1 << B, replace=(1 << B) > N) for _ in range(M)]).astype(np.int64)
+    cb, codes = E.aqlm_kmeans_init(torch.from_numpy(w).cuda(), torch.from_numpy(s).cuda(),
+                                   torch.from_numpy(seeds).cuda(), B, g, iters)
+    torch.cuda.synchronize()
+    cb_ref, codes_ref = O.kmeans_residual_init(w, s, seeds, M, B, g, iters)
+    np.testing.assert_array_equal(cb.cpu().numpy().view(np.uint16), cb_ref.view(np.uint16))
+    np.testing.assert_array_equal(codes.cpu().numpy(), codes_ref)
+
+
+def test_encode_and_kmeans_full_size_2x8():
+    """4096x4096 weights: encoder codes on sampled rows equal the oracle's; the k-means codes are the
+    greedy encoding against the k-means codebooks (checked on sampled rows)."""
+    w, s = weights(4096, 4096, seed=0)
+    wd, sd = torch.from_numpy(w).cuda(), torch.from_numpy(s).cuda()
+    cb = np.random.default_rng(3).normal(0, 1, size=(2, 256, 8)).astype(np.float16)
+    codes = E.aqlm_encode_greedy(wd, sd, torch.from_numpy(cb).cuda())
+    N = 4096 * 512
+    seeds = np.stack([np.random.default_rng(5 + m).choice(N, 256, replace=False) for m in range(2)])
+    kcb, kcodes = E.aqlm_kmeans_init(wd, sd, torch.from_numpy(seeds).cuda(), 8, 8, 2)
+    torch.cuda.synchronize()
+    rows = sample_rows(4096, 24)
+    np.testing.assert_array_equal(codes.cpu().numpy()[rows], O.encode_greedy(w[rows], s[rows], cb))
+    kcb = kcb.cpu().numpy()
+    np.testing.assert_array_equal(kcodes.cpu().numpy()[rows], O.encode_greedy(w[rows], s[rows], kcb))
+    # the k-means codebooks reconstruct the layer better than random codebooks of the same spread
+    err_km = np.abs(O.decode_fp32(kcodes.cpu().numpy()[rows], kcb, s[rows]) - w[rows].astype(np.float32)).mean()
+    err_rand = np.abs(O.decode_fp32(codes.cpu().numpy()[rows], cb, s[rows]) - w[rows].astype(np.float32)).mean()
+    assert err_km < err_rand
+
+
+# --------------------------------------------------------------------------
 # Errors through the binding
 
 
