@@ -29,10 +29,10 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_F16_PEAK_TFLOPS = 2500
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
 # fp32 vector ALU: 157.3 TFLOP/s counts a fused multiply-add as 2 flops, so a
 # plain (unfused) add, subtract or multiply peaks at half that op rate.
-VALU_F32_PEAK_TOPS = 157.3 / 2.0  # MI355X dense fp16 matrix cores
+VALU_F32_PEAK_TOPS = 157.3 / 2.0
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 
 BLOCK_7B = ((4096, 4096),) * 4 + ((11008, 4096),) * 2 + ((4096, 11008),)
