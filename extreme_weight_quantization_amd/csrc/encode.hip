@@ -29,6 +29,8 @@
 // differently and would change which codeword is nearest.  One thread owns one
 // group; the block streams the candidate codewords through LDS in 32 KB tiles,
 // which all lanes read at the same address (a broadcast).
+#include <algorithm>
+
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
@@ -42,6 +44,7 @@ constexpr int kEncThreads = 256;
 constexpr int kTileBytes = 32768;
 constexpr double kFixedPoint = 16777216.0;          // 2^24
 constexpr double kInvFixedPoint = 5.9604644775390625e-08;   // 2^-24
+constexpr size_t kLdsAccBytes = 98304;                      // k-means sums kept in LDS up to this size
 
 template <int CB>
 __device__ __forceinline__ uint32_t load_code(const uint8_t* codes, size_t i, uint32_t mask) {
@@ -79,8 +82,12 @@ __device__ __forceinline__ void residual(const f16* __restrict__ w, const f16* _
 // Assignment of every group to its nearest candidate for codebook m.
 //   FINAL  : candidates = fp16 codebook m; writes code m of the group.
 //   KMEANS : candidates = fp32 centroids; adds the group's fixed-point leftover
-//            to its cluster's sums and counts it.
-template <int G, int CB, bool KMEANS>
+//            to its cluster's sums and counts it.  With LACC the workgroup first
+//            sums into LDS (dynamic shared memory, K*(G+1) int64) over all of its
+//            groups and adds the non-zero totals to the global sums once at the
+//            end: integer sums do not depend on the order, and the global
+//            atomics drop from one per group to one per cluster and workgroup.
+template <int G, int CB, bool KMEANS, bool LACC = false>
 __global__ __launch_bounds__(kEncThreads) void assign_kernel(
     const f16* __restrict__ w, const f16* __restrict__ scales, const f16* __restrict__ codebooks,
     uint8_t* __restrict__ codes, const float* __restrict__ centroids, unsigned long long* __restrict__ sums,
@@ -88,8 +95,13 @@ __global__ __launch_bounds__(kEncThreads) void assign_kernel(
     int m) {
     constexpr int kTile = kTileBytes / (4 * G);   // candidates per LDS tile
     __shared__ float tile[kTile * G];
+    extern __shared__ unsigned long long lacc[];   // LACC: [K][G] sums, then [K] counts
     const int K = 1 << B;
     const f16* cbm = codebooks + ((size_t)m << B) * G;
+    if constexpr (LACC) {
+        for (int i = threadIdx.x; i < K * (G + 1); i += kEncThreads) lacc[i] = 0ull;
+        __syncthreads();
+    }
     for (int64_t base = (int64_t)blockIdx.x * kEncThreads; base < n_groups;
          base += (int64_t)gridDim.x * kEncThreads) {
         const int64_t n = base + threadIdx.x;
@@ -123,15 +135,24 @@ __global__ __launch_bounds__(kEncThreads) void assign_kernel(
         }
         if (active) {
             if constexpr (KMEANS) {
+                unsigned long long* ps = LACC ? lacc : sums;
+                unsigned long long* pc = LACC ? lacc + (size_t)K * G : counts;
 #pragma unroll
                 for (int t = 0; t < G; ++t) {
                     const long long q = __double2ll_rn((double)r[t] * kFixedPoint);
-                    atomicAdd(&sums[(size_t)best_k * G + t], (unsigned long long)q);
+                    atomicAdd(&ps[(size_t)best_k * G + t], (unsigned long long)q);
                 }
-                atomicAdd(&counts[best_k], 1ull);
+                atomicAdd(&pc[best_k], 1ull);
             } else {
                 store_code<CB>(codes, (size_t)n * M + m, (uint32_t)best_k);
             }
+        }
+    }
+    if constexpr (LACC) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < K * (G + 1); i += kEncThreads) {
+            const unsigned long long v = lacc[i];
+            if (v != 0ull) atomicAdd(i < K * G ? &sums[i] : &counts[i - K * G], v);
         }
     }
 }
@@ -224,9 +245,27 @@ hipError_t kmeans_g(const EncArgs& a, const int64_t* seeds, void* workspace, int
         for (int it = 0; it < iters; ++it) {
             hipLaunchKernelGGL(zero_kernel, dim3(grid_for((int64_t)K * (G + 1), kEncThreads)), dim3(kEncThreads), 0,
                                stream, sums, (int64_t)K * (G + 1));
-            hipLaunchKernelGGL((assign_kernel<G, CB, true>), dim3(grid_for(n, kEncThreads)), dim3(kEncThreads), 0,
-                               stream, a.w, a.scales, a.codebooks, a.codes, centroids, sums, counts, n, gpr,
-                               (int)a.in, a.M, a.B, m);
+            const size_t lacc_bytes = (size_t)K * (G + 1) * 8;
+            if (lacc_bytes <= kLdsAccBytes) {
+                // as many workgroups per compute unit as LDS holds (at most 4), each summing many groups in LDS
+                auto kern = assign_kernel<G, CB, true, true>;
+                if (lacc_bytes > 32768) {
+                    const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                             (int)lacc_bytes);
+                    if (e != hipSuccess) return e;
+                }
+                const int64_t need = (n + kEncThreads - 1) / kEncThreads;
+                const int64_t per_cu = std::min<int64_t>(4, std::max<int64_t>(1, 163840 / (kTileBytes + (int64_t)lacc_bytes)));
+                const int64_t cap = device_cu_count() * per_cu;
+                hipLaunchKernelGGL(kern, dim3((unsigned)(need < cap ? need : cap)), dim3(kEncThreads), lacc_bytes,
+                                   stream, a.w, a.scales, a.codebooks, a.codes, centroids, sums, counts, n, gpr,
+                                   (int)a.in, a.M, a.B, m);
+            } else {
+                hipLaunchKernelGGL((assign_kernel<G, CB, true>), dim3(grid_for(n, kEncThreads)), dim3(kEncThreads),
+                                   0, stream, a.w, a.scales, a.codebooks, a.codes, centroids, sums, counts, n, gpr,
+                                   (int)a.in, a.M, a.B, m);
+            }
             hipLaunchKernelGGL(update_kernel, dim3(grid_for((int64_t)K * G, kEncThreads)), dim3(kEncThreads), 0, stream,
                                sums, counts, centroids, (int64_t)K * G, G);
         }
