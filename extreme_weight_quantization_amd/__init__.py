@@ -7,6 +7,9 @@ is loaded on first use and its absence is an error: there is no fallback.
 """
 from .binding import (  # noqa: F401
     AqlmError,
+    SliceLists,
+    aqlm_linear_gemv_lists,
+    aqlm_lists_pack,
     aqlm_linear_decode,
     aqlm_linear_gemm,
     aqlm_linear_gemv,
@@ -14,6 +17,8 @@ from .binding import (  # noqa: F401
     aqlm_encode_greedy,
     aqlm_kmeans_init,
     kmeans_workspace_bytes,
+    lists_table_bytes,
+    lists_workspace_bytes,
     load_library,
     status_str,
 )

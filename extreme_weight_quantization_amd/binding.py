@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
+from dataclasses import dataclass
 
 import torch
 
@@ -18,7 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaqlm.so"
 AQLM_OK, AQLM_ERR_NULL, AQLM_ERR_SHAPE, AQLM_ERR_SCHEME, AQLM_ERR_ALIGN, AQLM_ERR_HIP = range(6)
 EXPORTED = ("aqlm_linear_gemv", "aqlm_linear_gemv_fused", "aqlm_linear_gemm", "aqlm_linear_decode",
             "aqlm_encode_greedy", "aqlm_kmeans_workspace_bytes", "aqlm_kmeans_init",
-            "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
+            "aqlm_lists_table_bytes", "aqlm_lists_workspace_bytes", "aqlm_lists_plan", "aqlm_lists_fill",
+            "aqlm_linear_gemv_lists", "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
 FUSED_MAX_LAYERS = 8   # AQLM_FUSED_MAX_LAYERS
 
 _lib = None
@@ -56,6 +58,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.aqlm_kmeans_workspace_bytes.restype = ci
         lib.aqlm_kmeans_init.argtypes = [vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, i64, i64, ci, vp]
         lib.aqlm_kmeans_init.restype = ci
+        for name in ("aqlm_lists_table_bytes", "aqlm_lists_workspace_bytes"):
+            getattr(lib, name).argtypes = [ci, ci, ci, i64, i64, ctypes.POINTER(i64)]
+            getattr(lib, name).restype = ci
+        lib.aqlm_lists_plan.argtypes = [vp, vp, ci, ci, ci, i64, i64, vp]
+        lib.aqlm_lists_plan.restype = ci
+        lib.aqlm_lists_fill.argtypes = [vp, vp, vp, i64, ci, ci, ci, i64, i64, vp]
+        lib.aqlm_lists_fill.restype = ci
+        lib.aqlm_linear_gemv_lists.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, ci, ci, ci, i64, i64, i64, vp]
+        lib.aqlm_linear_gemv_lists.restype = ci
         lib.aqlm_status_str.argtypes = [ci]
         lib.aqlm_status_str.restype = ctypes.c_char_p
         lib.aqlm_last_hip_error.argtypes = []
@@ -271,6 +282,81 @@ def aqlm_kmeans_init(w, scales, seeds, B, g, iters, codebooks=None, codes=None, 
                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                                            M, B, g, out, n_in, int(iters), _stream(w.device)))
     return codebooks, codes
+
+
+def _lists_bytes(fn_name, out, n_in) -> int:
+    n = ctypes.c_int64(0)
+    _check(getattr(load_library(), fn_name)(1, 16, 8, int(out), int(n_in), ctypes.byref(n)))
+    return int(n.value)
+
+
+def lists_table_bytes(out, n_in) -> int:
+    """Bytes of the slice-list table of a 1x16 layer [out][n_in] (see aqlm.h)."""
+    return _lists_bytes("aqlm_lists_table_bytes", out, n_in)
+
+
+def lists_workspace_bytes(out, n_in) -> int:
+    """Bytes of workspace aqlm_linear_gemv_lists needs for a 1x16 layer [out][n_in]."""
+    return _lists_bytes("aqlm_lists_workspace_bytes", out, n_in)
+
+
+@dataclass
+class SliceLists:
+    """The codes of one 1x16 layer regrouped by codebook slice (layout in aqlm.h).
+
+    table and entries are uint8 GPU tensors holding the library's table and
+    entries; out and n_in are the layer's shape."""
+    table: torch.Tensor
+    entries: torch.Tensor
+    out: int
+    n_in: int
+
+    @property
+    def steps(self) -> int:
+        return self.entries.numel() // 256
+
+
+def aqlm_lists_pack(codes) -> SliceLists:
+    """Slice lists of 1x16 codes [out][in/8][1] (int16): plan, read the size, allocate, fill.
+
+    Synchronises the current stream once (to read the number of entries)."""
+    if not (codes.is_cuda and codes.is_contiguous() and codes.dtype == torch.int16 and codes.dim() == 3
+            and codes.shape[2] == 1):
+        raise ValueError("codes must be a contiguous int16 GPU tensor [out][in/8][1]")
+    out, n_in = int(codes.shape[0]), int(codes.shape[1]) * 8
+    lib = load_library()
+    table = torch.empty(lists_table_bytes(out, n_in), dtype=torch.uint8, device=codes.device)
+    stream = _stream(codes.device)
+    _check(lib.aqlm_lists_plan(_ptr(codes), _ptr(table), 1, 16, 8, out, n_in, stream))
+    torch.cuda.current_stream(codes.device).synchronize()
+    steps = int(table[-8:].cpu().view(torch.int64).item())
+    entries = torch.empty(steps * 256, dtype=torch.uint8, device=codes.device)
+    _check(lib.aqlm_lists_fill(_ptr(codes), _ptr(table), _ptr(entries), entries.numel(), 1, 16, 8, out, n_in,
+                               stream))
+    return SliceLists(table, entries, out, n_in)
+
+
+def aqlm_linear_gemv_lists(lists: SliceLists, codebooks, scales, x, y=None, workspace=None):
+    """y = W x at batch 1 over slice lists (see aqlm.h); x is [1][in] (or [0][in])."""
+    for name, t in (("codebooks", codebooks), ("scales", scales), ("x", x)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float16:
+            raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
+    if codebooks.shape != (1, 1 << 16, 8):
+        raise ValueError("codebooks must be [1][65536][8]")
+    if x.dim() != 2 or x.shape[1] != lists.n_in or x.shape[0] > 1:
+        raise ValueError(f"x must be [1][{lists.n_in}]")
+    batch = int(x.shape[0])
+    if y is None:
+        y = torch.empty((batch, lists.out), dtype=torch.float16, device=x.device)
+    elif y.shape != (batch, lists.out) or y.dtype != torch.float16 or not y.is_contiguous():
+        raise ValueError(f"y must be a contiguous float16 [{batch}][{lists.out}] tensor")
+    if workspace is None:
+        workspace = torch.empty(lists_workspace_bytes(lists.out, lists.n_in), dtype=torch.uint8, device=x.device)
+    _check(load_library().aqlm_linear_gemv_lists(
+        _ptr(lists.table), _ptr(lists.entries), lists.entries.numel(), _ptr(codebooks), _ptr(scales), _ptr(x),
+        _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(), 1, 16, 8, lists.out, lists.n_in,
+        batch, _stream(x.device)))
+    return y
 
 
 def raw_call_fused(n_layers, codes, codebooks, scales, outs, x, ys, M, B, g, n_in, batch, stream=0) -> int:

@@ -202,6 +202,65 @@ int aqlm_kmeans_init(const void* w, const void* scales, const int64_t* seeds, vo
                                      (hipStream_t)stream));
 }
 
+// ---- 1x16 slice lists
+static int validate_lists(int M, int B, int g, int64_t out, int64_t in) {
+    if (!(M == 1 && B == 16 && g == 8)) return AQLM_ERR_SCHEME;
+    if (out < 0 || out > AQLM_LISTS_MAX_OUT || in < 8 || in > AQLM_MAX_IN || (in % 8) != 0) return AQLM_ERR_SHAPE;
+    if ((uint64_t)out * (uint64_t)(in / 8) > (uint64_t)UINT32_MAX) return AQLM_ERR_SHAPE;
+    return AQLM_OK;
+}
+
+int aqlm_lists_table_bytes(int M, int B, int g, int64_t out, int64_t in, int64_t* bytes) {
+    if (!bytes) return AQLM_ERR_NULL;
+    const int st = validate_lists(M, B, g, out, in);
+    if (st != AQLM_OK) return st;
+    *bytes = lists_table_bytes(out, in);
+    return AQLM_OK;
+}
+
+int aqlm_lists_workspace_bytes(int M, int B, int g, int64_t out, int64_t in, int64_t* bytes) {
+    if (!bytes) return AQLM_ERR_NULL;
+    const int st = validate_lists(M, B, g, out, in);
+    if (st != AQLM_OK) return st;
+    *bytes = lists_workspace_bytes(out, in);
+    return AQLM_OK;
+}
+
+int aqlm_lists_plan(const void* codes, void* table, int M, int B, int g, int64_t out, int64_t in, void* stream) {
+    const int st = validate_lists(M, B, g, out, in);
+    if (st != AQLM_OK) return st;
+    if (!table || (out > 0 && !codes)) return AQLM_ERR_NULL;
+    if (!aligned(table, 16) || (codes && !aligned(codes, 16))) return AQLM_ERR_ALIGN;
+    return finish(launch_lists_plan(codes, out, in, table, (hipStream_t)stream));
+}
+
+int aqlm_lists_fill(const void* codes, const void* table, void* entries, int64_t entries_bytes, int M, int B, int g,
+                    int64_t out, int64_t in, void* stream) {
+    const int st = validate_lists(M, B, g, out, in);
+    if (st != AQLM_OK) return st;
+    if (entries_bytes < 0) return AQLM_ERR_SHAPE;
+    if (out == 0) return AQLM_OK;
+    if (!codes || !table || !entries) return AQLM_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(table, 16) || !aligned(entries, 16)) return AQLM_ERR_ALIGN;
+    return finish(launch_lists_fill(codes, out, in, table, entries, entries_bytes, (hipStream_t)stream));
+}
+
+int aqlm_linear_gemv_lists(const void* table, const void* entries, int64_t entries_bytes, const void* codebooks,
+                           const void* scales, const void* x, void* y, void* workspace, int64_t workspace_bytes, int M,
+                           int B, int g, int64_t out, int64_t in, int64_t batch, void* stream) {
+    const int st = validate_lists(M, B, g, out, in);
+    if (st != AQLM_OK) return st;
+    if (batch < 0 || batch > 1 || entries_bytes < 0 || workspace_bytes < 0) return AQLM_ERR_SHAPE;
+    if (out == 0 || batch == 0) return AQLM_OK;
+    if (!table || !entries || !codebooks || !scales || !x || !y || !workspace) return AQLM_ERR_NULL;
+    if (!aligned(table, 16) || !aligned(entries, 16) || !aligned(codebooks, 16) || !aligned(x, 16) ||
+        !aligned(y, 16) || !aligned(workspace, 16) || !aligned(scales, 2))
+        return AQLM_ERR_ALIGN;
+    if (workspace_bytes < lists_workspace_bytes(out, in)) return AQLM_ERR_SHAPE;
+    return finish(launch_gemv_lists(table, entries, entries_bytes, codebooks, scales, x, y, workspace, out, in,
+                                    (hipStream_t)stream));
+}
+
 const char* aqlm_status_str(int status) {
     switch (status) {
         case AQLM_OK: return "AQLM_OK";

@@ -66,4 +66,30 @@ hipError_t launch_gemm(int scheme, const void* codes, const void* codebooks, con
                        const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                        hipStream_t stream);
 
+// 1x16 products over slice lists (gemv_lists.hip): codes regrouped by codebook
+// slice per 64-row tile and per block of at most kListsMaxBlock groups.  The
+// geometry depends on (out, in) only.
+constexpr int kListsMaxBlock = 1024;
+struct ListsGeo {
+    int G;      // groups per row (in / 8)
+    int J;      // blocks of groups
+    int Gb;     // groups per block (the last may have fewer)
+    int Z;      // Gb rounded up to 64: index of the zero x chunk that padding entries name
+    int n_rt;   // 64-row tiles
+    int W;      // workgroups per (slice, block)
+    int R;      // row tiles per workgroup (at most)
+    int P;      // parts the steps of a unit are split into
+    __host__ __device__ int64_t n_units() const { return (int64_t)8 * J * n_rt; }
+    __host__ __device__ int slots() const { return 8 * J * P; }
+};
+ListsGeo lists_geo(int64_t out, int64_t in);
+int64_t lists_table_bytes(int64_t out, int64_t in);
+int64_t lists_workspace_bytes(int64_t out, int64_t in);
+hipError_t launch_lists_plan(const void* codes, int64_t out, int64_t in, void* table, hipStream_t stream);
+hipError_t launch_lists_fill(const void* codes, int64_t out, int64_t in, const void* table, void* entries,
+                             int64_t entries_bytes, hipStream_t stream);
+hipError_t launch_gemv_lists(const void* table, const void* entries, int64_t entries_bytes, const void* codebook,
+                             const void* scales, const void* x, void* y, void* workspace, int64_t out, int64_t in,
+                             hipStream_t stream);
+
 }  // namespace aqlm

@@ -1,0 +1,330 @@
+// Decode-phase product for the 1x16 scheme at batch 1 over "slice lists": the
+// codes of a layer regrouped once, at load time, by codebook slice.
+//
+// "The AQLM Quantization Algorithm, Explained", section "Why and what do we
+// quantize?": decoding is memory-bound, and dequantization overhead can eat
+// the gain.  For 1x16 (section "Key AQLM quantization parameters": 2^16
+// codewords, the slower scheme) that overhead is the lookup: a 16-byte
+// codeword gathered from the 1 MiB codebook costs one L2 request, and L2
+// requests, not HBM, bound a kernel that gathers per code.
+//
+// Here the codebook is cut into 8 slices of 8192 codewords (128 KB each), and
+// a workgroup holds one slice in LDS, so no lookup leaves the CU.  For that to
+// pay, a workgroup must read only the codes of its slice, which the row-major
+// code array does not allow; hence the layout built by aqlm_lists_plan and
+// aqlm_lists_fill from the plain codes:
+//
+//   rows form tiles of 64 (lane l of a wave serves row 64 rt + l); the groups
+//   j of a row form J blocks of at most 1024 groups (block k starts at
+//   k * Gb); for every (slice s, block k, row tile rt) unit, each row lists
+//   its codes c with c >> 13 == s and j in block k, in ascending j, as 32-bit
+//   entries ((j - k Gb) << 13) | (c & 8191).  The 64 lists of a unit are
+//   padded to the longest one, L, with the entry Z << 13 (Z: the block size
+//   rounded up to 64; x chunk Z is zero in LDS), and stored step-major:
+//   entry t of row l at entries[(off + t) * 64 + l].
+//
+//   table (uint32): for unit u = (s * J + k) * n_rt + rt, table[2u] = off
+//   (in steps of 64 entries) and table[2u + 1] = L; then the total number of
+//   steps as a uint64 at word 2 * n_units.
+//
+// Nothing is lost: the multiset of (row, j, code) triples is the code array.
+// The product then reads every entry once (coalesced 256-byte steps), looks
+// up its codeword and its 8 activations in LDS, and accumulates in fp32 per
+// lane (one row per lane: no cross-lane reduction).  Every (unit, part)
+// writes one fp32 partial per row; a second kernel adds a row's partials in
+// a fixed order, applies the scale and rounds to fp16 once.
+#include <algorithm>
+
+#include "aqlm_device.h"
+#include "aqlm_launch.h"
+
+namespace aqlm {
+
+namespace {
+
+constexpr int kSlices = 8;
+constexpr int kSliceBits = 13;
+constexpr int kSliceWords = 1 << kSliceBits;     // codewords per slice: 128 KB of LDS
+constexpr int kListThreads = 1024;
+constexpr int kListWaves = kListThreads / kWave;
+constexpr int kListRing = 8;                     // entry loads in flight per lane
+constexpr int kWgPerSlice = 32;                  // workgroups per (slice, block): 256 in all
+constexpr int kReduceParts = 4;                  // threads per row in the partial sum
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
+    return (__attribute__((address_space(3))) void*)p;
+}
+
+// 8 fp16 weights times 8 fp16 activations, accumulated in fp32 two products
+// at a time (v_dot2_f32_f16, no rounding between the two products).
+__device__ __forceinline__ float dot8(const u32x4 w, const u32x4 xv, float acc) {
+    const f16x8 a = as_f16x8(w), b = as_f16x8(xv);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f16x2 pa, pb;
+        pa[0] = a[2 * q];
+        pa[1] = a[2 * q + 1];
+        pb[0] = b[2 * q];
+        pb[1] = b[2 * q + 1];
+        acc = __builtin_amdgcn_fdot2(pa, pb, acc, false);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// ---- plan: L of every unit (one wave per unit; lane = row)
+__global__ __launch_bounds__(256) void lists_count_kernel(const uint16_t* __restrict__ codes, int out,
+                                                          ListsGeo geo, uint32_t* __restrict__ table) {
+    const int lane = threadIdx.x & 63;
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (u >= geo.n_units()) return;
+    const int rt = (int)(u % geo.n_rt);
+    const int k = (int)((u / geo.n_rt) % geo.J);
+    const int s = (int)(u / ((int64_t)geo.n_rt * geo.J));
+    const int row = rt * 64 + lane;
+    const int j0 = k * geo.Gb, j1 = min(geo.G, j0 + geo.Gb);
+    int n = 0;
+    if (row < out) {
+        const uint16_t* c = codes + (size_t)row * geo.G;
+        for (int j = j0; j < j1; ++j) n += (c[j] >> kSliceBits) == s;
+    }
+    n = wave_max(n);
+    if (lane == 0) table[2 * u + 1] = (uint32_t)n;
+}
+
+// ---- plan: offsets (exclusive prefix of L in unit order) and the total, one workgroup
+__global__ __launch_bounds__(1024) void lists_scan_kernel(ListsGeo geo, uint32_t* __restrict__ table) {
+    __shared__ uint64_t wsum[16];
+    __shared__ uint64_t carry_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n = geo.n_units();
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < n; base += 1024) {
+        const int64_t u = base + tid;
+        const uint64_t L = u < n ? table[2 * u + 1] : 0;
+        uint64_t incl = L;   // inclusive scan within the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint64_t v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        uint64_t before = carry_s;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        if (u < n) table[2 * u] = (uint32_t)(before + incl - L);
+        __syncthreads();
+        if (tid == 1023) carry_s = before + incl;
+        __syncthreads();
+    }
+    if (tid == 0) *reinterpret_cast<uint64_t*>(table + 2 * n) = carry_s;
+}
+
+// ---- fill: one wave per unit writes its 64 lists, padded to L
+__global__ __launch_bounds__(256) void lists_fill_kernel(const uint16_t* __restrict__ codes, int out, ListsGeo geo,
+                                                         const uint32_t* __restrict__ table,
+                                                         uint32_t* __restrict__ entries, uint64_t cap_steps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (u >= geo.n_units()) return;
+    const uint64_t off = table[2 * u], L = table[2 * u + 1];
+    if (off + L > cap_steps) return;   // not the table of this layer: leave the entries alone
+    const int rt = (int)(u % geo.n_rt);
+    const int k = (int)((u / geo.n_rt) % geo.J);
+    const int s = (int)(u / ((int64_t)geo.n_rt * geo.J));
+    const int row = rt * 64 + lane;
+    const int j0 = k * geo.Gb, j1 = min(geo.G, j0 + geo.Gb);
+    uint32_t* e = entries + off * 64 + lane;
+    uint64_t t = 0;
+    if (row < out) {
+        const uint16_t* c = codes + (size_t)row * geo.G;
+        for (int j = j0; j < j1 && t < L; ++j) {
+            const uint32_t code = c[j];
+            if ((int)(code >> kSliceBits) == s) {
+                e[t * 64] = ((uint32_t)(j - j0) << kSliceBits) | (code & (kSliceWords - 1));
+                ++t;
+            }
+        }
+    }
+    for (; t < L; ++t) e[t * 64] = (uint32_t)geo.Z << kSliceBits;
+}
+
+// ---- the product
+__global__ __launch_bounds__(kListThreads) void gemv_lists_kernel(const uint32_t* __restrict__ table,
+                                                                  const uint32_t* __restrict__ entries,
+                                                                  uint64_t cap_steps, const f16* __restrict__ codebook,
+                                                                  const f16* __restrict__ x,
+                                                                  float* __restrict__ partial, ListsGeo geo) {
+    extern __shared__ u32x4 smem[];
+    u32x4* cbs = smem;                 // the slice: kSliceWords codewords
+    u32x4* xs = smem + kSliceWords;    // the x block: Z + 1 chunks of 8 fp16, chunk Z = 0
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // workgroup -> (slice, block, index among the workgroups of the pair); consecutive
+    // workgroups go to different XCDs, so the workgroups of an XCD share one slice in its L2
+    const int s = blockIdx.x % kSlices;
+    const int rest = blockIdx.x / kSlices;
+    const int k = rest % geo.J, wi = rest / geo.J;
+    const int out_pad = geo.n_rt * 64;
+
+    // slice and x block into LDS (lane l of a wave writes 16 bytes at base + 16 l)
+    {
+        const u32x4* src = reinterpret_cast<const u32x4*>(codebook) + (size_t)s * kSliceWords;
+#pragma unroll
+        for (int i = 0; i < kSliceWords / kListThreads; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(src + i * kListThreads + tid),
+                                             lds_ptr(cbs + i * kListThreads + wave * 64), 16, 0, 0);
+        const int j0 = k * geo.Gb;
+        const int nk = min(geo.G - j0, geo.Gb);   // chunks of this block; whole waves of 64 are copied
+        const u32x4* xsrc = reinterpret_cast<const u32x4*>(x) + j0;
+        if (wave * 64 < nk)
+            __builtin_amdgcn_global_load_lds((const void*)(xsrc + min(tid, nk - 1)), lds_ptr(xs + wave * 64), 16, 0,
+                                             0);
+        if (tid == 0) xs[geo.Z] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // units (r, p) of this workgroup: its r-th row tile, p-th of P equal parts of the steps
+    const int n_units = geo.R * geo.P;
+    bool waited = false;
+    for (int uu = wave; uu < n_units; uu += kListWaves) {
+        const int r = uu / geo.P, p = uu % geo.P;
+        const int rt = wi + r * geo.W;
+        if (rt >= geo.n_rt) break;
+        const int64_t unit = ((int64_t)s * geo.J + k) * geo.n_rt + rt;
+        const uint64_t off = table[2 * unit];
+        uint64_t L = table[2 * unit + 1];
+        if (off + L > cap_steps) L = 0;   // a table that does not fit the entries reads nothing
+        const int t0 = (int)((uint64_t)p * L / geo.P), t1 = (int)((uint64_t)(p + 1) * L / geo.P);
+        const int n = t1 - t0;
+        const uint32_t* e = entries + off * 64 + lane;
+        auto fetch = [&](int t) -> uint32_t { return e[(size_t)min(t0 + t, t1 - 1) * 64]; };
+        uint32_t ring[kListRing];
+#pragma unroll
+        for (int i = 0; i < kListRing; ++i) ring[i] = n > 0 ? fetch(i) : 0u;
+        if (!waited) {   // the LDS fill (issued before the ring) has landed in every wave
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            waited = true;
+        }
+        float acc = 0.f;
+        for (int base = 0; base < n; base += kListRing) {
+#pragma unroll
+            for (int i = 0; i < kListRing; ++i) {
+                const uint32_t en = ring[i];
+                ring[i] = fetch(base + i + kListRing);   // clamped to the unit's last step
+                if (base + i < n)
+                    acc = dot8(cbs[en & (kSliceWords - 1)], xs[min((int)(en >> kSliceBits), geo.Z)], acc);
+            }
+        }
+        const int slot = (s * geo.J + k) * geo.P + p;
+        partial[(size_t)slot * out_pad + rt * 64 + lane] = acc;
+    }
+    if (!waited) {   // no unit: the barrier is still everyone's
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+}
+
+// y[r] = fp16(s[r] * sum of the row's partials), the slots split into kReduceParts
+// contiguous runs added in slot order, then the runs in order.
+__global__ __launch_bounds__(64 * kReduceParts) void lists_reduce_kernel(const float* __restrict__ partial,
+                                                                         const f16* __restrict__ scales,
+                                                                         f16* __restrict__ y, int out, int out_pad,
+                                                                         int slots) {
+    __shared__ float red[kReduceParts][64];
+    const int rl = threadIdx.x & 63, part = threadIdx.x >> 6;
+    const int r = blockIdx.x * 64 + rl;
+    const int per = (slots + kReduceParts - 1) / kReduceParts;
+    const int q0 = min(slots, part * per), q1 = min(slots, q0 + per);
+    float sum = 0.f;
+    if (r < out) {
+        for (int qb = q0; qb < q1; qb += 16) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = qb + i < q1 ? partial[(size_t)(qb + i) * out_pad + r] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sum += v[i];
+        }
+    }
+    red[part][rl] = sum;
+    __syncthreads();
+    if (part == 0 && r < out) {
+        float t = red[0][rl];
+#pragma unroll
+        for (int q = 1; q < kReduceParts; ++q) t += red[q][rl];
+        y[r] = (f16)(t * (float)scales[r]);
+    }
+}
+
+}  // namespace
+
+ListsGeo lists_geo(int64_t out, int64_t in) {
+    ListsGeo g;
+    g.G = (int)(in / 8);
+    g.J = (g.G + kListsMaxBlock - 1) / kListsMaxBlock;
+    g.Gb = (g.G + g.J - 1) / g.J;
+    g.Z = (g.Gb + 63) / 64 * 64;
+    g.n_rt = (int)((out + 63) / 64);
+    g.W = std::max(1, std::min(kWgPerSlice / g.J, g.n_rt));
+    g.R = (g.n_rt + g.W - 1) / g.W;
+    g.P = g.R > 0 ? std::max(1, kListWaves / g.R) : 1;   // out == 0: no row tiles
+    return g;
+}
+
+int64_t lists_table_bytes(int64_t out, int64_t in) {
+    const ListsGeo g = lists_geo(out, in);
+    return (2 * g.n_units() + 2) * 4;
+}
+
+int64_t lists_workspace_bytes(int64_t out, int64_t in) {
+    const ListsGeo g = lists_geo(out, in);
+    return (int64_t)g.slots() * g.n_rt * 64 * 4;
+}
+
+hipError_t launch_lists_plan(const void* codes, int64_t out, int64_t in, void* table, hipStream_t stream) {
+    const ListsGeo g = lists_geo(out, in);
+    const int64_t blocks = (g.n_units() + 3) / 4;
+    if (blocks > 0)
+        hipLaunchKernelGGL(lists_count_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(codes), (int)out, g, static_cast<uint32_t*>(table));
+    hipLaunchKernelGGL(lists_scan_kernel, dim3(1), dim3(1024), 0, stream, g, static_cast<uint32_t*>(table));
+    return hipGetLastError();
+}
+
+hipError_t launch_lists_fill(const void* codes, int64_t out, int64_t in, const void* table, void* entries,
+                             int64_t entries_bytes, hipStream_t stream) {
+    const ListsGeo g = lists_geo(out, in);
+    const int64_t blocks = (g.n_units() + 3) / 4;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(lists_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(codes), (int)out, g, static_cast<const uint32_t*>(table),
+                       static_cast<uint32_t*>(entries), (uint64_t)(entries_bytes / 256));
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_lists(const void* table, const void* entries, int64_t entries_bytes, const void* codebook,
+                             const void* scales, const void* x, void* y, void* workspace, int64_t out, int64_t in,
+                             hipStream_t stream) {
+    const ListsGeo g = lists_geo(out, in);
+    const size_t lds = (size_t)kSliceWords * 16 + (size_t)(g.Z + 1) * 16;
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_lists_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    float* partial = static_cast<float*>(workspace);
+    const int64_t grid = (int64_t)kSlices * g.J * g.W;
+    hipLaunchKernelGGL(gemv_lists_kernel, dim3((unsigned)grid), dim3(kListThreads), lds, stream,
+                       static_cast<const uint32_t*>(table), static_cast<const uint32_t*>(entries),
+                       (uint64_t)(entries_bytes / 256), static_cast<const f16*>(codebook),
+                       static_cast<const f16*>(x), partial, g);
+    hipLaunchKernelGGL(lists_reduce_kernel, dim3((unsigned)((out + 63) / 64)), dim3(64 * kReduceParts), 0, stream,
+                       partial, static_cast<const f16*>(scales), static_cast<f16*>(y), (int)out, g.n_rt * 64,
+                       g.slots());
+    return hipGetLastError();
+}
+
+}  // namespace aqlm

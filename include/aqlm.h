@@ -173,6 +173,59 @@ int aqlm_kmeans_init(const void* w, const void* scales, const int64_t* seeds, vo
                      void* workspace, int64_t workspace_bytes, int M, int B, int g,
                      int64_t out, int64_t in, int iters, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * 1x16 at batch 1 over slice lists ("Key AQLM quantization parameters" on the
+ * same page: 1x16 is the scheme with 2^16 codewords, and its decoding is the
+ * slower one because of them).  The product above gathers a 16-byte codeword
+ * per code from the 1 MiB codebook; these calls instead regroup the codes of
+ * a layer once, at load time, so that a workgroup can keep one eighth of the
+ * codebook (8192 codewords, 128 KB) in LDS and read only the codes that fall
+ * in it.  Only (M, B, g) = (1, 16, 8) (else AQLM_ERR_SCHEME); 8 <= in <=
+ * AQLM_MAX_IN, in % 8 == 0, out <= AQLM_LISTS_MAX_OUT and out * in/8 <=
+ * 2^32 - 1 (else AQLM_ERR_SHAPE).
+ *
+ * Layout (all device memory, 16-byte aligned, owned by the caller):
+ *   rows form tiles of 64; the groups j of a row form J = ceil(G / 1024)
+ *   blocks of Gb = ceil(G / J) groups (G = in / 8); for every unit
+ *   u = (s * J + k) * ceil(out / 64) + rt (slice s < 8, block k, row tile
+ *   rt), row 64 rt + l lists its codes c with c >> 13 == s and j in block k,
+ *   ascending in j, as uint32 entries ((j - k Gb) << 13) | (c & 8191); the
+ *   64 lists are padded to the longest, L, with Z << 13 (Z = Gb rounded up
+ *   to a multiple of 64) and stored as entries[(off + t) * 64 + l].
+ *   table: uint32 pairs (off, L) per unit, then the total number of steps
+ *   (sum of L) as a uint64; entries take 256 bytes per step.
+ *
+ * Building: aqlm_lists_plan(codes, table) writes the table (asynchronous);
+ * the caller reads the total (the uint64 at byte aqlm_lists_table_bytes - 8)
+ * after synchronising, allocates total * 256 bytes of entries and calls
+ * aqlm_lists_fill.  A fill or product whose entries_bytes is smaller than a
+ * unit's off + L needs leaves that unit out (no access beyond entries_bytes);
+ * a table that does not belong to the codes gives wrong results, never an
+ * access outside the buffers.  The product needs a caller workspace of
+ * aqlm_lists_workspace_bytes (fp32 partial sums, overwritten by every call;
+ * calls that share a workspace must not run concurrently).
+ *
+ * Result: y = W x for batch 1 (batch 0 enqueues nothing), accumulated in
+ * fp32, rounded to fp16 once; deterministic (the summation order is fixed by
+ * out and in), but not bit-identical to aqlm_linear_gemv, which adds in
+ * another order.
+ */
+#define AQLM_LISTS_MAX_OUT (1 << 30)
+
+/* Bytes of the table of a layer (into *bytes). */
+int aqlm_lists_table_bytes(int M, int B, int g, int64_t out, int64_t in, int64_t* bytes);
+/* Bytes of workspace aqlm_linear_gemv_lists needs for the shape (into *bytes). */
+int aqlm_lists_workspace_bytes(int M, int B, int g, int64_t out, int64_t in, int64_t* bytes);
+/* Writes the table of codes [out][in/8] (int16) into table.  codes may be NULL when out == 0. */
+int aqlm_lists_plan(const void* codes, void* table, int M, int B, int g, int64_t out, int64_t in, void* stream);
+/* Writes the entries of codes, placed by table, into entries (entries_bytes long). */
+int aqlm_lists_fill(const void* codes, const void* table, void* entries, int64_t entries_bytes, int M, int B, int g,
+                    int64_t out, int64_t in, void* stream);
+/* y[0][i] = sum_k W[i][k] x[0][k] over the slice lists (codebooks, scales, x, y as for aqlm_linear_gemv). */
+int aqlm_linear_gemv_lists(const void* table, const void* entries, int64_t entries_bytes, const void* codebooks,
+                           const void* scales, const void* x, void* y, void* workspace, int64_t workspace_bytes, int M,
+                           int B, int g, int64_t out, int64_t in, int64_t batch, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* aqlm_status_str(int status);
 

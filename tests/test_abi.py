@@ -215,3 +215,88 @@ def test_binding_rejects_cpu_tensors(lib):
         E.aqlm_linear_gemv(codes, cb, s, x)
     with pytest.raises(ValueError):
         E.aqlm_linear_decode(codes, cb, s)
+
+
+# --------------------------------------------------------------------------
+# 1x16 slice lists
+
+
+def lists_geometry_sizes(out, n_in):
+    """Table and workspace bytes from the layout's definition (tiles of 64 rows, blocks of <= 1024 groups)."""
+    G = n_in // 8
+    J = -(-G // 1024)
+    n_rt = -(-out // 64)
+    W = max(1, min(32 // J, n_rt))
+    R = -(-n_rt // W)
+    P = max(1, 16 // R) if R else 1
+    return (2 * 8 * J * n_rt + 2) * 4, 8 * J * P * n_rt * 64 * 4
+
+
+@pytest.mark.parametrize("out,n_in", [(4096, 4096), (11008, 4096), (4096, 11008), (28672, 8192), (8192, 28672),
+                                      (1024, 8192), (1, 8), (130, 72), (0, 64)])
+def test_lists_sizes(lib, out, n_in):
+    table, ws = lists_geometry_sizes(out, n_in)
+    assert binding.lists_table_bytes(out, n_in) == table
+    assert binding.lists_workspace_bytes(out, n_in) == ws
+
+
+def test_lists_size_validation(lib):
+    import ctypes as C
+    n = C.c_int64(0)
+    for name in ("aqlm_lists_table_bytes", "aqlm_lists_workspace_bytes"):
+        fn = lib_fn(name)
+        assert fn(1, 16, 8, 64, 512, C.byref(n)) == binding.AQLM_OK
+        assert fn(2, 8, 8, 64, 512, C.byref(n)) == binding.AQLM_ERR_SCHEME
+        assert fn(1, 16, 4, 64, 512, C.byref(n)) == binding.AQLM_ERR_SCHEME
+        assert fn(1, 16, 8, 64, 500, C.byref(n)) == binding.AQLM_ERR_SHAPE
+        assert fn(1, 16, 8, 64, 0, C.byref(n)) == binding.AQLM_ERR_SHAPE
+        assert fn(1, 16, 8, -1, 512, C.byref(n)) == binding.AQLM_ERR_SHAPE
+        assert fn(1, 16, 8, (1 << 30) + 1, 8, C.byref(n)) == binding.AQLM_ERR_SHAPE
+        assert fn(1, 16, 8, 1 << 20, 1 << 19, C.byref(n)) == binding.AQLM_ERR_SHAPE   # 2^36 codes
+        assert fn(1, 16, 8, 64, 512, None) == binding.AQLM_ERR_NULL
+
+
+def lists_gemv(**kw):
+    a = dict(table=A, entries=A, entries_bytes=1 << 20, cb=A, scales=A, x=A, y=A, ws=A, ws_bytes=1 << 30,
+             M=1, B=16, g=8, out=64, n_in=512, batch=1)
+    a.update(kw)
+    return int(lib_fn("aqlm_linear_gemv_lists")(a["table"], a["entries"], a["entries_bytes"], a["cb"], a["scales"],
+                                                a["x"], a["y"], a["ws"], a["ws_bytes"], a["M"], a["B"], a["g"],
+                                                a["out"], a["n_in"], a["batch"], None))
+
+
+def test_validation_gemv_lists(lib):
+    for key in ("table", "entries", "cb", "scales", "x", "y", "ws"):
+        assert lists_gemv(**{key: 0}) == binding.AQLM_ERR_NULL
+    assert lists_gemv(M=2, B=8) == binding.AQLM_ERR_SCHEME
+    assert lists_gemv(batch=2) == binding.AQLM_ERR_SHAPE
+    assert lists_gemv(batch=-1) == binding.AQLM_ERR_SHAPE
+    assert lists_gemv(n_in=520 + 4) == binding.AQLM_ERR_SHAPE
+    assert lists_gemv(entries_bytes=-1) == binding.AQLM_ERR_SHAPE
+    assert lists_gemv(ws_bytes=lists_geometry_sizes(64, 512)[1] - 1) == binding.AQLM_ERR_SHAPE
+    for key in ("table", "entries", "cb", "x", "y", "ws"):
+        assert lists_gemv(**{key: A + 8}) == binding.AQLM_ERR_ALIGN
+    assert lists_gemv(scales=A + 1) == binding.AQLM_ERR_ALIGN
+    assert lists_gemv(batch=0, table=0, entries=0, x=0, y=0) == binding.AQLM_OK
+    assert lists_gemv(out=0, table=0, ws=0) == binding.AQLM_OK
+
+
+def test_validation_lists_plan_and_fill(lib):
+    plan, fill = lib_fn("aqlm_lists_plan"), lib_fn("aqlm_lists_fill")
+    assert plan(A, None, 1, 16, 8, 64, 512, None) == binding.AQLM_ERR_NULL
+    assert plan(None, A, 1, 16, 8, 64, 512, None) == binding.AQLM_ERR_NULL
+    assert plan(A, A + 8, 1, 16, 8, 64, 512, None) == binding.AQLM_ERR_ALIGN
+    assert plan(A, A, 2, 8, 8, 64, 512, None) == binding.AQLM_ERR_SCHEME
+    assert plan(A, A, 1, 16, 8, 64, 12, None) == binding.AQLM_ERR_SHAPE
+    for args in ((None, A, A), (A, None, A), (A, A, None)):
+        assert fill(*args, 1 << 20, 1, 16, 8, 64, 512, None) == binding.AQLM_ERR_NULL
+    assert fill(A, A, A + 4, 1 << 20, 1, 16, 8, 64, 512, None) == binding.AQLM_ERR_ALIGN
+    assert fill(A, A, A, -1, 1, 16, 8, 64, 512, None) == binding.AQLM_ERR_SHAPE
+    assert fill(A, A, A, 1 << 20, 1, 12, 4, 64, 512, None) == binding.AQLM_ERR_SCHEME
+    assert fill(None, None, None, 0, 1, 16, 8, 0, 512, None) == binding.AQLM_OK
+
+
+def test_binding_lists_rejects_bad_codes(lib):
+    import torch
+    with pytest.raises(ValueError):
+        E.aqlm_lists_pack(torch.zeros((4, 8, 1), dtype=torch.int16))           # CPU tensor
