@@ -4,16 +4,21 @@
 Headline workload: the seven projections of one Llama-2-7B decoder block
 (q, k, v, o 4096x4096; gate, up 11008x4096; down 4096x11008) as AQLM 1x16
 (one 65536-entry fp16 codebook, int16 codes, g = 8) decode-phase GEMVs at
-batch 1.  One step runs all seven layers once.  The reported value is the
-achieved HBM bandwidth over the counted bytes (codes + scales + activations
-+ outputs), with inputs resident in HBM and rotated over enough distinct
-buffer sets to defeat the 256 MB last-level cache.
+batch 1.  One step runs all seven layers once, each as one
+aqlm_linear_gemv_lists call over the layer's slice lists (its codes regrouped
+by codebook slice once, at load time, before any timed region).  The reported
+value is the achieved HBM bandwidth over the counted bytes (codes at 2 bits
+per weight + scales + activations + outputs), with inputs resident in HBM and
+rotated over enough distinct buffer sets to defeat the 256 MB last-level
+cache.
 
-Also measured in the same run (reported under "breakdown", not in value):
-2x8 GEMV at batch 1/4/16 on the same block, the Llama-2-70B 1x16 layers at
-batch 1, the 2048-token prefill GEMM on the 7B shapes (both schemes) and the
-standalone decode kernel.  The CPU oracle is timed on the host on one of each
-7B layer shape.
+Also measured in the same run (reported under "breakdown", not in value): the
+same block with the codes in their stored layout (aqlm_linear_gemv, per-code
+codebook gathers), alone and with q,k,v and gate,up fused; 2x8 GEMV at batch
+1/4/16 on the same block; the Llama-2-70B 1x16 layers at batch 1 in both
+layouts; the 2048-token prefill GEMM on the 7B shapes (both schemes); the
+standalone decode kernel; the other 2-bit schemes; the encoder; and the fp16
+comparator.  The CPU oracle is timed on the host over whole block steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 Prints one JSON line on stdout.
@@ -110,6 +115,15 @@ class LayerSet:
                                torch.empty((batch, out), dtype=torch.float16, device="cuda")))
             self.sets.append(layers)
         self.bytes_per_step = sum(gemv_bytes(o, i, batch) for o, i in shapes)
+        self.lists = None
+
+    def pack_lists(self, torch, E):
+        """Slice lists of every 1x16 layer (the load-time regrouping; never inside a timed region)."""
+        self.lists = [[E.aqlm_lists_pack(codes) for (codes, _, _, _) in layers] for layers in self.sets]
+        self.ws = torch.empty(max(E.lists_workspace_bytes(o, i) for o, i in self.shapes), dtype=torch.uint8,
+                              device="cuda")
+        torch.cuda.synchronize()
+        return sum(l.entries.numel() for l in self.lists[0])
 
 
 def sets_needed(shapes, batch, min_bytes=4 * LLC_BYTES, cap=64):
@@ -151,12 +165,16 @@ def replay_us(torch, graph, reps=1):
     return a.elapsed_time(b) * 1e3
 
 
-def gemv_launches(E, ls, k0, n_steps, only=None):
+def gemv_launches(E, ls, k0, n_steps, only=None, lists=False):
     out = []
     for k in range(k0, k0 + n_steps):
         for li, (codes, s, x, y) in enumerate(ls.sets[k % len(ls.sets)]):
             if only is None or ls.shapes[li] == only:
-                out.append(lambda c=codes, s=s, x=x, y=y: E.aqlm_linear_gemv(c, ls.cb, s, x, y))
+                if lists:
+                    lst = ls.lists[k % len(ls.sets)][li]
+                    out.append(lambda l=lst, s=s, x=x, y=y: E.aqlm_linear_gemv_lists(l, ls.cb, s, x, y, ls.ws))
+                else:
+                    out.append(lambda c=codes, s=s, x=x, y=y: E.aqlm_linear_gemv(c, ls.cb, s, x, y))
     return out
 
 
@@ -191,7 +209,7 @@ def time_fused_block(torch, E, ls: LayerSet, steps, warmup):
     return ms_step
 
 
-def time_gemv(torch, E, ls: LayerSet, steps, warmup):
+def time_gemv(torch, E, ls: LayerSet, steps, warmup, lists=False):
     """Times exactly `steps` passes over the layer list (rotating buffer sets).
 
     The launches are captured in a HIP graph so that the device runs them
@@ -199,14 +217,14 @@ def time_gemv(torch, E, ls: LayerSet, steps, warmup):
     HIP events.  Per-shape kernel durations come from graphs of back-to-back
     launches of one shape.  Returns (ms per step, {shape: us per launch}).
     """
-    g_warm = capture(torch, gemv_launches(E, ls, 0, max(1, warmup)))
-    g_main = capture(torch, gemv_launches(E, ls, warmup, steps))
+    g_warm = capture(torch, gemv_launches(E, ls, 0, max(1, warmup), lists=lists))
+    g_main = capture(torch, gemv_launches(E, ls, warmup, steps, lists=lists))
     replay_us(torch, g_warm)
     ms_step = replay_us(torch, g_main) / steps / 1e3
     per_shape = {}
     for shape in dict.fromkeys(ls.shapes):
         n = max(1, min(len(ls.sets), 64))
-        g = capture(torch, gemv_launches(E, ls, 0, n, only=shape))
+        g = capture(torch, gemv_launches(E, ls, 0, n, only=shape, lists=lists))
         count = n * ls.shapes.count(shape)
         replay_us(torch, g)
         per_shape[shape] = replay_us(torch, g, reps=4) / (4 * count)
@@ -226,13 +244,16 @@ def time_calls(torch, launch, iters, warmup):
     return us
 
 
-def spot_check(torch, E, ls: LayerSet, rows_per_layer=32):
+def spot_check(torch, E, ls: LayerSet, rows_per_layer=32, lists=False):
     """Compares sampled outputs of set 0 with the CPU oracle (parity of the timed launches)."""
     from oracle import aqlm_oracle as O
     worst = 0.0
     cb = ls.cb.cpu().numpy()
-    for (codes, s, x, y) in ls.sets[0]:
-        E.aqlm_linear_gemv(codes, ls.cb, s, x, y)
+    for li, (codes, s, x, y) in enumerate(ls.sets[0]):
+        if lists:
+            E.aqlm_linear_gemv_lists(ls.lists[0][li], ls.cb, s, x, y, ls.ws)
+        else:
+            E.aqlm_linear_gemv(codes, ls.cb, s, x, y)
         torch.cuda.synchronize()
         out = codes.shape[0]
         rows = np.unique(np.linspace(0, out - 1, rows_per_layer).astype(np.int64))
@@ -244,19 +265,20 @@ def spot_check(torch, E, ls: LayerSet, rows_per_layer=32):
     return worst
 
 
-def recorded_traffic():
-    """Per-launch HBM bytes of gemv_kernel<1x16> from the committed rocprofv3 PMC record.
+def recorded_traffic(record="gemv_lists_1x16_llama2_7b_block_b1_traffic.json",
+                     sources=("gemv_lists.hip", "aqlm_device.h")):
+    """Per-launch HBM bytes of the headline kernels from a committed rocprofv3 PMC record.
 
     Returned only while the kernel sources hash to the value recorded with the
     counters; a changed kernel reports None until the counters are taken again.
     """
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
-    rec_path = os.path.join(root, "profiles", "gemv_1x16_llama2_7b_block_b1_traffic.json")
+    rec_path = os.path.join(root, "profiles", record)
     try:
         rec = json.load(open(rec_path))
         h = hashlib.sha256()
-        for f in ("gemv.hip", "aqlm_device.h"):
+        for f in sources:
             h.update(open(os.path.join(root, "extreme_weight_quantization_amd", "csrc", f), "rb").read())
         if h.hexdigest()[:16] != rec["source_sha256_16"]:
             return None
@@ -320,28 +342,43 @@ def main():
     torch.cuda.init()
     dev_name = torch.cuda.get_device_name(0)
 
-    # ---- headline: 7B block, 1x16, batch 1 ---------------------------------
+    # ---- headline: 7B block, 1x16, batch 1, codes as slice lists -----------
     n_sets = sets_needed(BLOCK_7B, 1)
     ls = LayerSet(torch, "1x16", BLOCK_7B, 1, n_sets, seed=0)
-    worst = spot_check(torch, E, ls)
+    entry_bytes_step = ls.pack_lists(torch, E)
+    worst = spot_check(torch, E, ls, lists=True)
     torch.cuda.synchronize()
-    ms_step, shape_us = time_gemv(torch, E, ls, args.steps, args.warmup)
+    ms_step, shape_us = time_gemv(torch, E, ls, args.steps, args.warmup, lists=True)
     value = ls.bytes_per_step / (ms_step * 1e-3) / 1e9
     kern_us_step = sum(shape_us[sh] for sh in BLOCK_7B)
     achieved = ls.bytes_per_step / (kern_us_step * 1e-6) / 1e9
-    per_shape = {f"{o}x{i}": {"us": round(us, 3), "GBps": round(gemv_bytes(o, i, 1) / (us * 1e-6) / 1e9, 1),
-                              "pct_hbm_peak": round(100 * gemv_bytes(o, i, 1) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
-                 for (o, i), us in shape_us.items()}
+
+    def shape_table(su, batch=1):
+        return {f"{o}x{i}": {"us": round(us, 3), "GBps": round(gemv_bytes(o, i, batch) / (us * 1e-6) / 1e9, 1),
+                             "pct_hbm_peak": round(100 * gemv_bytes(o, i, batch) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+                for (o, i), us in su.items()}
+
+    per_shape = shape_table(shape_us)
+    breakdown = {"gemv_1x16_b1_7b": per_shape}
     fused = {}
     if not args.quick:
+        # the same layers and buffers with the codes in their stored layout (per-code L2 gathers)
+        worst_plain = spot_check(torch, E, ls)
+        ms_plain, shape_plain = time_gemv(torch, E, ls, args.steps, args.warmup)
+        kp = sum(shape_plain[sh] for sh in BLOCK_7B)
+        breakdown["gemv_1x16_b1_7b_stored_layout"] = {
+            "ms_per_step": round(ms_plain, 5), "us_per_layer": round(ms_plain * 1e3 / len(BLOCK_7B), 3),
+            "GBps_step": round(ls.bytes_per_step / (ms_plain * 1e-3) / 1e9, 1),
+            "GBps_kernel": round(ls.bytes_per_step / (kp * 1e-6) / 1e9, 1),
+            "spot_check_rel_l2": worst_plain, "per_shape": shape_table(shape_plain)}
         ms_f = time_fused_block(torch, E, ls, max(20, args.steps // 2), 5)
-        fused["1x16_b1"] = {"ms_per_step": round(ms_f, 5), "us_per_layer": round(ms_f * 1e3 / len(BLOCK_7B), 3),
-                            "GBps_step": round(ls.bytes_per_step / (ms_f * 1e-3) / 1e9, 1),
-                            "unfused_ms_per_step": round(ms_step, 5)}
+        fused["1x16_b1_stored_layout"] = {"ms_per_step": round(ms_f, 5),
+                                          "us_per_layer": round(ms_f * 1e3 / len(BLOCK_7B), 3),
+                                          "GBps_step": round(ls.bytes_per_step / (ms_f * 1e-3) / 1e9, 1),
+                                          "unfused_ms_per_step": round(ms_plain, 5)}
     del ls
     torch.cuda.empty_cache()
 
-    breakdown = {"gemv_1x16_b1_7b": per_shape}
     if not args.quick:
         iters = max(20, args.steps // 2)
         # 2x8 GEMV on the 7B block at batch 1, 4, 16
@@ -369,10 +406,15 @@ def main():
         r70 = {}
         for shape in SHAPES_70B:
             ls3 = LayerSet(torch, "1x16", (shape,), 1, sets_needed((shape,), 1, cap=16), seed=2)
-            _, sh3 = time_gemv(torch, E, ls3, iters, 5)
-            k3 = sh3[shape]
-            r70[f"{shape[0]}x{shape[1]}"] = {"us": round(k3, 3),
-                                             "GBps": round(ls3.bytes_per_step / (k3 * 1e-6) / 1e9, 1)}
+            ls3.pack_lists(torch, E)
+            _, sh3 = time_gemv(torch, E, ls3, iters, 5, lists=True)
+            _, sh3p = time_gemv(torch, E, ls3, iters, 5)
+            k3, k3p = sh3[shape], sh3p[shape]
+            r70[f"{shape[0]}x{shape[1]}"] = {
+                "us": round(k3, 3), "GBps": round(ls3.bytes_per_step / (k3 * 1e-6) / 1e9, 1),
+                "pct_hbm_peak": round(100 * ls3.bytes_per_step / (k3 * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                "stored_layout_us": round(k3p, 3),
+                "stored_layout_GBps": round(ls3.bytes_per_step / (k3p * 1e-6) / 1e9, 1)}
             del ls3
             torch.cuda.empty_cache()
         breakdown["gemv_1x16_b1_70b"] = r70
@@ -458,6 +500,7 @@ def main():
         # denominator of the "speedup vs FP16" figures the AQLM pages quote.
         cmp16 = {}
         aq1 = {k: v["us"] for k, v in per_shape.items()}
+        aq1p = {k: v["us"] for k, v in breakdown["gemv_1x16_b1_7b_stored_layout"]["per_shape"].items()}
         aq2 = breakdown["gemv_2x8_b1_7b_block"]["per_shape"]
         for out, n_in in SHAPES_7B:
             n = max(2, min(32, -(-LLC_BYTES * 2 // (2 * out * n_in))))
@@ -468,6 +511,7 @@ def main():
             key = f"{out}x{n_in}"
             cmp16[key] = {"fp16_us": round(us16, 3),
                           "speedup_1x16": round(us16 / aq1[key], 3),
+                          "speedup_1x16_stored_layout": round(us16 / aq1p[key], 3),
                           "speedup_2x8": round(us16 / aq2[key]["us"], 3)}
             del ws16
             torch.cuda.empty_cache()
@@ -500,6 +544,9 @@ def main():
             "workload": "Llama-2-7B decoder-block projections (q,k,v,o 4096x4096; gate,up 11008x4096; "
                         "down 4096x11008) as AQLM 1x16 g8 decode GEMV, batch 1",
             "scheme": "1x16", "group": 8, "batch": 1, "layers_per_step": len(BLOCK_7B),
+            "codes_layout": "slice lists (aqlm_lists_pack once per layer at load, outside the timed region; "
+                            "the stored layout's figures are under breakdown)",
+            "entry_bytes_per_step": int(entry_bytes_step),
             "rotated_buffer_sets": n_sets, "parallelism": "single GPU",
             "us_per_layer": round(ms_step * 1e3 / len(BLOCK_7B), 3),
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -508,7 +555,8 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "kernel": "gemv_kernel<1x16>", "kernel_us_per_step": round(kern_us_step, 3),
+                     "kernel": "gemv_lists_kernel + lists_reduce_kernel (one aqlm_linear_gemv_lists call)",
+                     "kernel_us_per_step": round(kern_us_step, 3),
                      "method": "per-shape mean duration of back-to-back launches replayed from a HIP graph"},
         "cpu_baseline": cpu,
         "breakdown": breakdown,

@@ -80,7 +80,7 @@ struct ListsGeo {
     int R;      // row tiles per workgroup (at most)
     int P;      // parts the steps of a unit are split into
     __host__ __device__ int64_t n_units() const { return (int64_t)8 * J * n_rt; }
-    __host__ __device__ int slots() const { return 8 * J * P; }
+    __host__ __device__ int slots() const { return 8 * J; }   // partial sums per row
 };
 ListsGeo lists_geo(int64_t out, int64_t in);
 int64_t lists_table_bytes(int64_t out, int64_t in);

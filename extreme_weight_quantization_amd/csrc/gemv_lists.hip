@@ -30,9 +30,11 @@
 // Nothing is lost: the multiset of (row, j, code) triples is the code array.
 // The product then reads every entry once (coalesced 256-byte steps), looks
 // up its codeword and its 8 activations in LDS, and accumulates in fp32 per
-// lane (one row per lane: no cross-lane reduction).  Every (unit, part)
-// writes one fp32 partial per row; a second kernel adds a row's partials in
-// a fixed order, applies the scale and rounds to fp16 once.
+// lane (one row per lane: no cross-lane reduction).  When a row tile's steps
+// are split over P waves of a workgroup, their sums are added in LDS in part
+// order; every unit then writes one fp32 partial per row, and a second kernel
+// adds a row's 8 J partials in a fixed order, applies the scale and rounds to
+// fp16 once.
 #include <algorithm>
 
 #include "aqlm_device.h"
@@ -164,6 +166,7 @@ __global__ __launch_bounds__(kListThreads) void gemv_lists_kernel(const uint32_t
     extern __shared__ u32x4 smem[];
     u32x4* cbs = smem;                 // the slice: kSliceWords codewords
     u32x4* xs = smem + kSliceWords;    // the x block: Z + 1 chunks of 8 fp16, chunk Z = 0
+    float* red = reinterpret_cast<float*>(xs + geo.Z + 1);   // P > 1: the R * P unit sums, 64 per unit
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // workgroup -> (slice, block, index among the workgroups of the pair); consecutive
     // workgroups go to different XCDs, so the workgroups of an XCD share one slice in its L2
@@ -203,30 +206,52 @@ __global__ __launch_bounds__(kListThreads) void gemv_lists_kernel(const uint32_t
         const int n = t1 - t0;
         const uint32_t* e = entries + off * 64 + lane;
         auto fetch = [&](int t) -> uint32_t { return e[(size_t)min(t0 + t, t1 - 1) * 64]; };
-        uint32_t ring[kListRing];
+        uint32_t ring[kListRing] = {};
+        if (n > 0) {
 #pragma unroll
-        for (int i = 0; i < kListRing; ++i) ring[i] = n > 0 ? fetch(i) : 0u;
+            for (int i = 0; i < kListRing; ++i) ring[i] = fetch(i);
+        }
         if (!waited) {   // the LDS fill (issued before the ring) has landed in every wave
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             waited = true;
         }
         float acc = 0.f;
-        for (int base = 0; base < n; base += kListRing) {
+        int base = 0;
+        // whole chunks: all 2 * kListRing LDS reads are in flight before the first product
+        for (; base + kListRing <= n; base += kListRing) {
+            u32x4 w[kListRing], xv[kListRing];
 #pragma unroll
             for (int i = 0; i < kListRing; ++i) {
                 const uint32_t en = ring[i];
                 ring[i] = fetch(base + i + kListRing);   // clamped to the unit's last step
-                if (base + i < n)
-                    acc = dot8(cbs[en & (kSliceWords - 1)], xs[min((int)(en >> kSliceBits), geo.Z)], acc);
+                w[i] = cbs[en & (kSliceWords - 1)];
+                xv[i] = xs[min((int)(en >> kSliceBits), geo.Z)];
             }
+#pragma unroll
+            for (int i = 0; i < kListRing; ++i) acc = dot8(w[i], xv[i], acc);
         }
-        const int slot = (s * geo.J + k) * geo.P + p;
-        partial[(size_t)slot * out_pad + rt * 64 + lane] = acc;
+#pragma unroll
+        for (int i = 0; i < kListRing; ++i)   // the last n % kListRing steps, in order
+            if (base + i < n)
+                acc = dot8(cbs[ring[i] & (kSliceWords - 1)], xs[min((int)(ring[i] >> kSliceBits), geo.Z)], acc);
+        if (geo.P > 1)
+            red[uu * 64 + lane] = acc;
+        else
+            partial[(size_t)(s * geo.J + k) * out_pad + rt * 64 + lane] = acc;
     }
     if (!waited) {   // no unit: the barrier is still everyone's
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    }
+    if (geo.P > 1) {   // R * P <= 16: each wave had at most one unit; wave r adds the P parts of row tile r
+        __syncthreads();
+        const int rt = wi + wave * geo.W;
+        if (wave < geo.R && rt < geo.n_rt) {
+            float acc = red[wave * geo.P * 64 + lane];
+            for (int p = 1; p < geo.P; ++p) acc += red[(wave * geo.P + p) * 64 + lane];
+            partial[(size_t)(s * geo.J + k) * out_pad + rt * 64 + lane] = acc;
+        }
     }
 }
 
@@ -311,7 +336,7 @@ hipError_t launch_gemv_lists(const void* table, const void* entries, int64_t ent
                              const void* scales, const void* x, void* y, void* workspace, int64_t out, int64_t in,
                              hipStream_t stream) {
     const ListsGeo g = lists_geo(out, in);
-    const size_t lds = (size_t)kSliceWords * 16 + (size_t)(g.Z + 1) * 16;
+    const size_t lds = (size_t)kSliceWords * 16 + (size_t)(g.Z + 1) * 16 + (g.P > 1 ? (size_t)g.R * g.P * 64 * 4 : 0);
     const hipError_t e = hipFuncSetAttribute((const void*)gemv_lists_kernel,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

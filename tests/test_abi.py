@@ -226,10 +226,7 @@ def lists_geometry_sizes(out, n_in):
     G = n_in // 8
     J = -(-G // 1024)
     n_rt = -(-out // 64)
-    W = max(1, min(32 // J, n_rt))
-    R = -(-n_rt // W)
-    P = max(1, 16 // R) if R else 1
-    return (2 * 8 * J * n_rt + 2) * 4, 8 * J * P * n_rt * 64 * 4
+    return (2 * 8 * J * n_rt + 2) * 4, 8 * J * n_rt * 64 * 4
 
 
 @pytest.mark.parametrize("out,n_in", [(4096, 4096), (11008, 4096), (4096, 11008), (28672, 8192), (8192, 28672),
