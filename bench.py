@@ -120,8 +120,12 @@ class LayerSet:
     def pack_lists(self, torch, E):
         """Slice lists of every 1x16 layer (the load-time regrouping; never inside a timed region)."""
         self.lists = [[E.aqlm_lists_pack(codes) for (codes, _, _, _) in layers] for layers in self.sets]
-        self.ws = torch.empty(max(E.lists_workspace_bytes(o, i) for o, i in self.shapes), dtype=torch.uint8,
-                              device="cuda")
+        # one workspace for single calls and for the fused groups of the 7B block (the largest need)
+        need = max(E.lists_workspace_bytes(o, i) for o, i in self.shapes)
+        if self.shapes == BLOCK_7B:
+            need = max([need] + [E.lists_fused_workspace_bytes([self.shapes[i][0] for i in grp], self.shapes[grp[0]][1])
+                                 for grp in BLOCK_7B_GROUPS])
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
         return sum(l.entries.numel() for l in self.lists[0])
 
@@ -182,14 +186,23 @@ def gemv_launches(E, ls, k0, n_steps, only=None, lists=False):
 BLOCK_7B_GROUPS = ((0, 1, 2), (3,), (4, 5), (6,))
 
 
-def fused_block_launches(E, ls, k0, n_steps):
+def fused_block_launches(E, ls, k0, n_steps, lists=False):
     """One pass over the block per step with the projections that share x fused into one launch."""
     out = []
     for k in range(k0, k0 + n_steps):
         layers = ls.sets[k % len(ls.sets)]
         for grp in BLOCK_7B_GROUPS:
             x = layers[grp[0]][2]
-            if len(grp) == 1:
+            if lists:
+                lst = ls.lists[k % len(ls.sets)]
+                if len(grp) == 1:
+                    _, s, _, y = layers[grp[0]]
+                    out.append(lambda l=lst[grp[0]], s=s, x=x, y=y: E.aqlm_linear_gemv_lists(l, ls.cb, s, x, y, ls.ws))
+                else:
+                    lay = [(lst[i], ls.cb, layers[i][1]) for i in grp]
+                    ys = [layers[i][3] for i in grp]
+                    out.append(lambda lay=lay, x=x, ys=ys: E.aqlm_linear_gemv_lists_fused(lay, x, ys, ls.ws))
+            elif len(grp) == 1:
                 codes, s, _, y = layers[grp[0]]
                 out.append(lambda c=codes, s=s, x=x, y=y: E.aqlm_linear_gemv(c, ls.cb, s, x, y))
             else:
@@ -199,10 +212,10 @@ def fused_block_launches(E, ls, k0, n_steps):
     return out
 
 
-def time_fused_block(torch, E, ls: LayerSet, steps, warmup):
+def time_fused_block(torch, E, ls: LayerSet, steps, warmup, lists=False):
     """ms per 7B block step with fused projections (same rotation and graph timing as time_gemv)."""
-    g_warm = capture(torch, fused_block_launches(E, ls, 0, max(1, warmup)))
-    g_main = capture(torch, fused_block_launches(E, ls, warmup, steps))
+    g_warm = capture(torch, fused_block_launches(E, ls, 0, max(1, warmup), lists))
+    g_main = capture(torch, fused_block_launches(E, ls, warmup, steps, lists))
     replay_us(torch, g_warm)
     ms_step = replay_us(torch, g_main) / steps / 1e3
     del g_warm, g_main
@@ -371,6 +384,10 @@ def main():
             "GBps_step": round(ls.bytes_per_step / (ms_plain * 1e-3) / 1e9, 1),
             "GBps_kernel": round(ls.bytes_per_step / (kp * 1e-6) / 1e9, 1),
             "spot_check_rel_l2": worst_plain, "per_shape": shape_table(shape_plain)}
+        ms_fl = time_fused_block(torch, E, ls, max(20, args.steps // 2), 5, lists=True)
+        fused["1x16_b1"] = {"ms_per_step": round(ms_fl, 5), "us_per_layer": round(ms_fl * 1e3 / len(BLOCK_7B), 3),
+                            "GBps_step": round(ls.bytes_per_step / (ms_fl * 1e-3) / 1e9, 1),
+                            "unfused_ms_per_step": round(ms_step, 5), "codes_layout": "slice lists"}
         ms_f = time_fused_block(torch, E, ls, max(20, args.steps // 2), 5)
         fused["1x16_b1_stored_layout"] = {"ms_per_step": round(ms_f, 5),
                                           "us_per_layer": round(ms_f * 1e3 / len(BLOCK_7B), 3),

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     AqlmError,
     SliceLists,
     aqlm_linear_gemv_lists,
+    aqlm_linear_gemv_lists_fused,
     aqlm_lists_pack,
     aqlm_linear_decode,
     aqlm_linear_gemm,
@@ -17,6 +18,7 @@ from .binding import (  # noqa: F401
     aqlm_encode_greedy,
     aqlm_kmeans_init,
     kmeans_workspace_bytes,
+    lists_fused_workspace_bytes,
     lists_table_bytes,
     lists_workspace_bytes,
     load_library,

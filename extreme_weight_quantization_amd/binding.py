@@ -20,7 +20,8 @@ AQLM_OK, AQLM_ERR_NULL, AQLM_ERR_SHAPE, AQLM_ERR_SCHEME, AQLM_ERR_ALIGN, AQLM_ER
 EXPORTED = ("aqlm_linear_gemv", "aqlm_linear_gemv_fused", "aqlm_linear_gemm", "aqlm_linear_decode",
             "aqlm_encode_greedy", "aqlm_kmeans_workspace_bytes", "aqlm_kmeans_init",
             "aqlm_lists_table_bytes", "aqlm_lists_workspace_bytes", "aqlm_lists_plan", "aqlm_lists_fill",
-            "aqlm_linear_gemv_lists", "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
+            "aqlm_linear_gemv_lists", "aqlm_linear_gemv_lists_fused", "aqlm_lists_fused_workspace_bytes",
+            "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
 FUSED_MAX_LAYERS = 8   # AQLM_FUSED_MAX_LAYERS
 
 _lib = None
@@ -67,6 +68,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.aqlm_lists_fill.restype = ci
         lib.aqlm_linear_gemv_lists.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, ci, ci, ci, i64, i64, i64, vp]
         lib.aqlm_linear_gemv_lists.restype = ci
+        lib.aqlm_linear_gemv_lists_fused.argtypes = [ci, pp, pp, ctypes.POINTER(i64), pp, pp, ctypes.POINTER(i64),
+                                                     vp, pp, vp, i64, ci, ci, ci, i64, i64, vp]
+        lib.aqlm_linear_gemv_lists_fused.restype = ci
+        lib.aqlm_lists_fused_workspace_bytes.argtypes = [ci, ctypes.POINTER(i64), ci, ci, ci, i64,
+                                                         ctypes.POINTER(i64)]
+        lib.aqlm_lists_fused_workspace_bytes.restype = ci
         lib.aqlm_status_str.argtypes = [ci]
         lib.aqlm_status_str.restype = ctypes.c_char_p
         lib.aqlm_last_hip_error.argtypes = []
@@ -357,6 +364,49 @@ def aqlm_linear_gemv_lists(lists: SliceLists, codebooks, scales, x, y=None, work
         _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(), 1, 16, 8, lists.out, lists.n_in,
         batch, _stream(x.device)))
     return y
+
+
+def lists_fused_workspace_bytes(outs, n_in) -> int:
+    """Bytes of workspace aqlm_linear_gemv_lists_fused needs for 1x16 layers with these outs."""
+    n = ctypes.c_int64(0)
+    c_outs = (ctypes.c_int64 * max(len(outs), 1))(*[int(o) for o in outs])
+    _check(load_library().aqlm_lists_fused_workspace_bytes(len(outs), c_outs, 1, 16, 8, int(n_in), ctypes.byref(n)))
+    return int(n.value)
+
+
+def aqlm_linear_gemv_lists_fused(layers, x, ys=None, workspace=None):
+    """[y_l] for layers l = (SliceLists, codebooks, scales) that all multiply x ([1][in]), in one launch."""
+    n = len(layers)
+    if not 1 <= n <= FUSED_MAX_LAYERS:
+        raise ValueError(f"1 to {FUSED_MAX_LAYERS} layers")
+    if not (x.is_cuda and x.is_contiguous() and x.dtype == torch.float16 and x.dim() == 2 and x.shape[0] <= 1):
+        raise ValueError("x must be a contiguous float16 GPU tensor [1][in]")
+    n_in, batch = int(x.shape[1]), int(x.shape[0])
+    for lists, cb, s in layers:
+        if lists.n_in != n_in:
+            raise ValueError("every layer must take x's width")
+        for name, t in (("codebooks", cb), ("scales", s)):
+            if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float16:
+                raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
+    outs = [lists.out for lists, _, _ in layers]
+    if ys is None:
+        ys = [torch.empty((batch, o), dtype=torch.float16, device=x.device) for o in outs]
+    for y, o in zip(ys, outs):
+        if y.shape != (batch, o) or y.dtype != torch.float16 or not y.is_contiguous():
+            raise ValueError(f"y must be a contiguous float16 [{batch}][{o}] tensor")
+    if workspace is None:
+        workspace = torch.empty(max(lists_fused_workspace_bytes(outs, n_in), 1), dtype=torch.uint8,
+                                device=x.device)
+
+    def arr(vals):
+        return (ctypes.c_void_p * n)(*vals)
+    i64 = ctypes.c_int64 * n
+    _check(load_library().aqlm_linear_gemv_lists_fused(
+        n, arr([l.table.data_ptr() for l, _, _ in layers]), arr([l.entries.data_ptr() for l, _, _ in layers]),
+        i64(*[l.entries.numel() for l, _, _ in layers]), arr([cb.data_ptr() for _, cb, _ in layers]),
+        arr([s.data_ptr() for _, _, s in layers]), i64(*outs), _ptr(x), arr([y.data_ptr() for y in ys]),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), 1, 16, 8, n_in, batch, _stream(x.device)))
+    return ys
 
 
 def raw_call_fused(n_layers, codes, codebooks, scales, outs, x, ys, M, B, g, n_in, batch, stream=0) -> int:

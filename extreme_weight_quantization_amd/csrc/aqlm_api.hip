@@ -261,6 +261,59 @@ int aqlm_linear_gemv_lists(const void* table, const void* entries, int64_t entri
                                     (hipStream_t)stream));
 }
 
+int aqlm_lists_fused_workspace_bytes(int n_layers, const int64_t* outs, int M, int B, int g, int64_t in,
+                                     int64_t* bytes) {
+    if (!bytes || !outs) return AQLM_ERR_NULL;
+    if (n_layers < 1 || n_layers > AQLM_FUSED_MAX_LAYERS) return AQLM_ERR_SHAPE;
+    int64_t total = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        const int st = validate_lists(M, B, g, outs[l], in);
+        if (st != AQLM_OK) return st;
+        if (outs[l] > 0) total += lists_workspace_bytes_aligned(outs[l], in);
+    }
+    *bytes = total;
+    return AQLM_OK;
+}
+
+int aqlm_linear_gemv_lists_fused(int n_layers, const void* const* tables, const void* const* entries,
+                                 const int64_t* entries_bytes, const void* const* codebooks, const void* const* scales,
+                                 const int64_t* outs, const void* x, void* const* ys, void* workspace,
+                                 int64_t workspace_bytes, int M, int B, int g, int64_t in, int64_t batch,
+                                 void* stream) {
+    if (n_layers < 1 || n_layers > AQLM_FUSED_MAX_LAYERS) return AQLM_ERR_SHAPE;
+    if (!tables || !entries || !entries_bytes || !codebooks || !scales || !outs || !ys) return AQLM_ERR_NULL;
+    if (batch < 0 || batch > 1 || workspace_bytes < 0) return AQLM_ERR_SHAPE;
+    ListsLayers L{};
+    int64_t need = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        const int st = validate_lists(M, B, g, outs[l], in);
+        if (st != AQLM_OK) return st;
+        if (entries_bytes[l] < 0) return AQLM_ERR_SHAPE;
+        if (outs[l] == 0 || batch == 0) continue;
+        if (!tables[l] || !entries[l] || !codebooks[l] || !scales[l] || !ys[l]) return AQLM_ERR_NULL;
+        if (!aligned(tables[l], 16) || !aligned(entries[l], 16) || !aligned(codebooks[l], 16) ||
+            !aligned(ys[l], 16) || !aligned(scales[l], 2))
+            return AQLM_ERR_ALIGN;
+        const int i = L.n++;
+        L.table[i] = static_cast<const uint32_t*>(tables[l]);
+        L.entries[i] = static_cast<const uint32_t*>(entries[l]);
+        L.cap[i] = (uint64_t)(entries_bytes[l] / 256);
+        L.codebook[i] = codebooks[l];
+        L.scales[i] = scales[l];
+        L.y[i] = ys[l];
+        L.out[i] = (int)outs[l];
+        L.partial[i] = reinterpret_cast<float*>(need);   // offset for now
+        need += lists_workspace_bytes_aligned(outs[l], in);
+    }
+    if (L.n == 0) return AQLM_OK;
+    if (!x || !workspace) return AQLM_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(workspace, 16)) return AQLM_ERR_ALIGN;
+    if (workspace_bytes < need) return AQLM_ERR_SHAPE;
+    for (int i = 0; i < L.n; ++i)
+        L.partial[i] = reinterpret_cast<float*>(static_cast<char*>(workspace) + reinterpret_cast<intptr_t>(L.partial[i]));
+    return finish(launch_gemv_lists_fused(L, x, in, (hipStream_t)stream));
+}
+
 const char* aqlm_status_str(int status) {
     switch (status) {
         case AQLM_OK: return "AQLM_OK";

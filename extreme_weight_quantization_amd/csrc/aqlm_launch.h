@@ -83,6 +83,30 @@ struct ListsGeo {
     __host__ __device__ int slots() const { return 8 * J; }   // partial sums per row
 };
 ListsGeo lists_geo(int64_t out, int64_t in);
+
+// Layers of one slice-list product launch: all share x and in; layer l has its
+// own table, entries (cap = entries_bytes / 256 steps), codebook, scales, y,
+// partial sums (fp32, 8 J * 64 n_rt) and geometry.  Product workgroups
+// [wg_end[l-1], wg_end[l]) and reduction blocks [blk_end[l-1], blk_end[l])
+// serve layer l; the launcher fills both.  Passed to the kernels by value.
+struct ListsLayers {
+    const uint32_t* table[kGemvMaxLayers];
+    const uint32_t* entries[kGemvMaxLayers];
+    uint64_t cap[kGemvMaxLayers];
+    const void* codebook[kGemvMaxLayers];
+    const void* scales[kGemvMaxLayers];
+    void* y[kGemvMaxLayers];
+    float* partial[kGemvMaxLayers];
+    ListsGeo geo[kGemvMaxLayers];
+    int out[kGemvMaxLayers];
+    int wg_end[kGemvMaxLayers];
+    int blk_end[kGemvMaxLayers];
+    int n;
+};
+// Bytes of fp32 partial sums of one layer, rounded up to 256 (a fused launch
+// places the layers' partials one after another in its workspace).
+int64_t lists_workspace_bytes_aligned(int64_t out, int64_t in);
+hipError_t launch_gemv_lists_fused(ListsLayers layers, const void* x, int64_t in, hipStream_t stream);
 int64_t lists_table_bytes(int64_t out, int64_t in);
 int64_t lists_workspace_bytes(int64_t out, int64_t in);
 hipError_t launch_lists_plan(const void* codes, int64_t out, int64_t in, void* table, hipStream_t stream);

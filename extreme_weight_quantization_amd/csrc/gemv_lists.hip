@@ -157,12 +157,26 @@ __global__ __launch_bounds__(256) void lists_fill_kernel(const uint16_t* __restr
     for (; t < L; ++t) e[t * 64] = (uint32_t)geo.Z << kSliceBits;
 }
 
-// ---- the product
-__global__ __launch_bounds__(kListThreads) void gemv_lists_kernel(const uint32_t* __restrict__ table,
-                                                                  const uint32_t* __restrict__ entries,
-                                                                  uint64_t cap_steps, const f16* __restrict__ codebook,
-                                                                  const f16* __restrict__ x,
-                                                                  float* __restrict__ partial, ListsGeo geo) {
+// Layer of block b from a table of cumulative ends, and the layer's first block
+// (branch-free over values already in scalar registers: one round trip to the
+// kernel arguments before the layer's own fields).
+__device__ __forceinline__ int layer_of(const int* end, int n, int b, int* base) {
+    int l = 0, first = 0;
+#pragma unroll
+    for (int i = 0; i < kGemvMaxLayers - 1; ++i) {
+        const bool past = (i < n - 1) & (b >= end[i]);
+        l += past;
+        first = past ? end[i] : first;
+    }
+    *base = first;
+    return l;
+}
+
+// ---- the product: workgroup bid of one layer
+__device__ __forceinline__ void lists_product(const uint32_t* __restrict__ table, const uint32_t* __restrict__ entries,
+                                              uint64_t cap_steps, const f16* __restrict__ codebook,
+                                              const f16* __restrict__ x, float* __restrict__ partial,
+                                              const ListsGeo geo, int bid) {
     extern __shared__ u32x4 smem[];
     u32x4* cbs = smem;                 // the slice: kSliceWords codewords
     u32x4* xs = smem + kSliceWords;    // the x block: Z + 1 chunks of 8 fp16, chunk Z = 0
@@ -170,8 +184,8 @@ __global__ __launch_bounds__(kListThreads) void gemv_lists_kernel(const uint32_t
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // workgroup -> (slice, block, index among the workgroups of the pair); consecutive
     // workgroups go to different XCDs, so the workgroups of an XCD share one slice in its L2
-    const int s = blockIdx.x % kSlices;
-    const int rest = blockIdx.x / kSlices;
+    const int s = bid % kSlices;
+    const int rest = bid / kSlices;
     const int k = rest % geo.J, wi = rest / geo.J;
     const int out_pad = geo.n_rt * 64;
 
@@ -255,15 +269,31 @@ __global__ __launch_bounds__(kListThreads) void gemv_lists_kernel(const uint32_t
     }
 }
 
+// A single layer: its arguments directly (one small argument block).
+__global__ __launch_bounds__(kListThreads) void gemv_lists_kernel(const uint32_t* __restrict__ table,
+                                                                  const uint32_t* __restrict__ entries,
+                                                                  uint64_t cap_steps, const f16* __restrict__ codebook,
+                                                                  const f16* __restrict__ x,
+                                                                  float* __restrict__ partial, ListsGeo geo) {
+    lists_product(table, entries, cap_steps, codebook, x, partial, geo, blockIdx.x);
+}
+
+// Several layers that share x: the workgroup's layer from the table.
+__global__ __launch_bounds__(kListThreads) void gemv_lists_fused_kernel(const ListsLayers L,
+                                                                        const f16* __restrict__ x) {
+    int first = 0;
+    const int l = layer_of(L.wg_end, L.n, blockIdx.x, &first);
+    lists_product(L.table[l], L.entries[l], L.cap[l], static_cast<const f16*>(L.codebook[l]), x, L.partial[l],
+                  L.geo[l], blockIdx.x - first);
+}
+
 // y[r] = fp16(s[r] * sum of the row's partials), the slots split into kReduceParts
 // contiguous runs added in slot order, then the runs in order.
-__global__ __launch_bounds__(64 * kReduceParts) void lists_reduce_kernel(const float* __restrict__ partial,
-                                                                         const f16* __restrict__ scales,
-                                                                         f16* __restrict__ y, int out, int out_pad,
-                                                                         int slots) {
+__device__ __forceinline__ void lists_reduce(const float* __restrict__ partial, const f16* __restrict__ scales,
+                                             f16* __restrict__ y, int out, int out_pad, int slots, int blk) {
     __shared__ float red[kReduceParts][64];
     const int rl = threadIdx.x & 63, part = threadIdx.x >> 6;
-    const int r = blockIdx.x * 64 + rl;
+    const int r = blk * 64 + rl;
     const int per = (slots + kReduceParts - 1) / kReduceParts;
     const int q0 = min(slots, part * per), q1 = min(slots, q0 + per);
     float sum = 0.f;
@@ -284,6 +314,20 @@ __global__ __launch_bounds__(64 * kReduceParts) void lists_reduce_kernel(const f
         for (int q = 1; q < kReduceParts; ++q) t += red[q][rl];
         y[r] = (f16)(t * (float)scales[r]);
     }
+}
+
+__global__ __launch_bounds__(64 * kReduceParts) void lists_reduce_kernel(const float* __restrict__ partial,
+                                                                         const f16* __restrict__ scales,
+                                                                         f16* __restrict__ y, int out, int out_pad,
+                                                                         int slots) {
+    lists_reduce(partial, scales, y, out, out_pad, slots, blockIdx.x);
+}
+
+__global__ __launch_bounds__(64 * kReduceParts) void lists_reduce_fused_kernel(const ListsLayers L) {
+    int first = 0;
+    const int l = layer_of(L.blk_end, L.n, blockIdx.x, &first);
+    lists_reduce(L.partial[l], static_cast<const f16*>(L.scales[l]), static_cast<f16*>(L.y[l]), L.out[l],
+                 L.geo[l].n_rt * 64, L.geo[l].slots(), blockIdx.x - first);
 }
 
 }  // namespace
@@ -332,24 +376,59 @@ hipError_t launch_lists_fill(const void* codes, int64_t out, int64_t in, const v
     return hipGetLastError();
 }
 
+int64_t lists_workspace_bytes_aligned(int64_t out, int64_t in) {
+    return (lists_workspace_bytes(out, in) + 255) / 256 * 256;
+}
+
+// The caller has filled every per-layer field but geo, wg_end and blk_end (out > 0 for every layer).
+hipError_t launch_gemv_lists_fused(ListsLayers L, const void* x, int64_t in, hipStream_t stream) {
+    size_t lds = 0;
+    int64_t wgs = 0, blks = 0;
+    for (int l = 0; l < L.n; ++l) {
+        const ListsGeo g = lists_geo(L.out[l], in);
+        L.geo[l] = g;
+        lds = std::max(lds, (size_t)kSliceWords * 16 + (size_t)(g.Z + 1) * 16 +
+                                (g.P > 1 ? (size_t)g.R * g.P * 64 * 4 : 0));
+        wgs += (int64_t)kSlices * g.J * g.W;
+        blks += (L.out[l] + 63) / 64;
+        if (wgs > INT32_MAX || blks > INT32_MAX) return hipErrorInvalidValue;
+        L.wg_end[l] = (int)wgs;
+        L.blk_end[l] = (int)blks;
+    }
+    const bool multi = L.n > 1;
+    const void* kern = multi ? (const void*)gemv_lists_fused_kernel : (const void*)gemv_lists_kernel;
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    if (multi) {
+        hipLaunchKernelGGL(gemv_lists_fused_kernel, dim3((unsigned)wgs), dim3(kListThreads), lds, stream, L,
+                           static_cast<const f16*>(x));
+        hipLaunchKernelGGL(lists_reduce_fused_kernel, dim3((unsigned)blks), dim3(64 * kReduceParts), 0, stream, L);
+    } else {   // one layer: the compact argument lists
+        const ListsGeo& g = L.geo[0];
+        hipLaunchKernelGGL(gemv_lists_kernel, dim3((unsigned)wgs), dim3(kListThreads), lds, stream, L.table[0],
+                           L.entries[0], L.cap[0], static_cast<const f16*>(L.codebook[0]),
+                           static_cast<const f16*>(x), L.partial[0], g);
+        hipLaunchKernelGGL(lists_reduce_kernel, dim3((unsigned)blks), dim3(64 * kReduceParts), 0, stream,
+                           static_cast<const float*>(L.partial[0]), static_cast<const f16*>(L.scales[0]),
+                           static_cast<f16*>(L.y[0]), L.out[0], g.n_rt * 64, g.slots());
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv_lists(const void* table, const void* entries, int64_t entries_bytes, const void* codebook,
                              const void* scales, const void* x, void* y, void* workspace, int64_t out, int64_t in,
                              hipStream_t stream) {
-    const ListsGeo g = lists_geo(out, in);
-    const size_t lds = (size_t)kSliceWords * 16 + (size_t)(g.Z + 1) * 16 + (g.P > 1 ? (size_t)g.R * g.P * 64 * 4 : 0);
-    const hipError_t e = hipFuncSetAttribute((const void*)gemv_lists_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    float* partial = static_cast<float*>(workspace);
-    const int64_t grid = (int64_t)kSlices * g.J * g.W;
-    hipLaunchKernelGGL(gemv_lists_kernel, dim3((unsigned)grid), dim3(kListThreads), lds, stream,
-                       static_cast<const uint32_t*>(table), static_cast<const uint32_t*>(entries),
-                       (uint64_t)(entries_bytes / 256), static_cast<const f16*>(codebook),
-                       static_cast<const f16*>(x), partial, g);
-    hipLaunchKernelGGL(lists_reduce_kernel, dim3((unsigned)((out + 63) / 64)), dim3(64 * kReduceParts), 0, stream,
-                       partial, static_cast<const f16*>(scales), static_cast<f16*>(y), (int)out, g.n_rt * 64,
-                       g.slots());
-    return hipGetLastError();
+    ListsLayers L{};
+    L.n = 1;
+    L.table[0] = static_cast<const uint32_t*>(table);
+    L.entries[0] = static_cast<const uint32_t*>(entries);
+    L.cap[0] = (uint64_t)(entries_bytes / 256);
+    L.codebook[0] = codebook;
+    L.scales[0] = scales;
+    L.y[0] = y;
+    L.partial[0] = static_cast<float*>(workspace);
+    L.out[0] = (int)out;
+    return launch_gemv_lists_fused(L, x, in, stream);
 }
 
 }  // namespace aqlm

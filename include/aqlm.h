@@ -226,6 +226,28 @@ int aqlm_linear_gemv_lists(const void* table, const void* entries, int64_t entri
                            const void* scales, const void* x, void* y, void* workspace, int64_t workspace_bytes, int M,
                            int B, int g, int64_t out, int64_t in, int64_t batch, void* stream);
 
+/*
+ * n_layers slice-list products that share x (q/k/v, gate/up) in one launch of
+ * the product and one of the reduction: y_l = W_l x for l < n_layers, batch 1.
+ * tables, entries, entries_bytes, codebooks, scales, outs and ys are HOST
+ * arrays of n_layers entries (pointers in them are device pointers, laid out
+ * as for aqlm_linear_gemv_lists); the library reads them during the call.
+ * Each layer is validated as by aqlm_linear_gemv_lists; a layer with
+ * outs[l] == 0 is skipped.  workspace (16-byte aligned) holds the layers'
+ * partial sums one after another, each rounded up to 256 bytes:
+ * aqlm_lists_fused_workspace_bytes gives its size.  Results are bit-identical to separate aqlm_linear_gemv_lists calls.
+ * 1 <= n_layers <= AQLM_FUSED_MAX_LAYERS (else AQLM_ERR_SHAPE); a NULL array
+ * gives AQLM_ERR_NULL.
+ */
+int aqlm_linear_gemv_lists_fused(int n_layers, const void* const* tables, const void* const* entries,
+                                 const int64_t* entries_bytes, const void* const* codebooks, const void* const* scales,
+                                 const int64_t* outs, const void* x, void* const* ys, void* workspace,
+                                 int64_t workspace_bytes, int M, int B, int g, int64_t in, int64_t batch,
+                                 void* stream);
+/* Bytes of workspace aqlm_linear_gemv_lists_fused needs for the layers' outs (host array). */
+int aqlm_lists_fused_workspace_bytes(int n_layers, const int64_t* outs, int M, int B, int g, int64_t in,
+                                     int64_t* bytes);
+
 /* Static, human-readable name of a status code. */
 const char* aqlm_status_str(int status);
 

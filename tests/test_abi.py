@@ -297,3 +297,49 @@ def test_binding_lists_rejects_bad_codes(lib):
     import torch
     with pytest.raises(ValueError):
         E.aqlm_lists_pack(torch.zeros((4, 8, 1), dtype=torch.int16))           # CPU tensor
+
+
+def lists_fused(n=2, **kw):
+    a = dict(tables=[A] * n, entries=[A] * n, eb=[1 << 20] * n, cbs=[A] * n, scales=[A] * n, outs=[64] * n, x=A,
+             ys=[A] * n, ws=A, ws_bytes=1 << 30, M=1, B=16, g=8, n_in=512, batch=1)
+    a.update(kw)
+    import ctypes as C
+
+    def arr(v):
+        return None if v is None else (C.c_void_p * max(len(v), 1))(*v)
+
+    def i64(v):
+        return None if v is None else (C.c_int64 * max(len(v), 1))(*v)
+    return int(lib_fn("aqlm_linear_gemv_lists_fused")(
+        n, arr(a["tables"]), arr(a["entries"]), i64(a["eb"]), arr(a["cbs"]), arr(a["scales"]), i64(a["outs"]),
+        a["x"], arr(a["ys"]), a["ws"], a["ws_bytes"], a["M"], a["B"], a["g"], a["n_in"], a["batch"], None))
+
+
+def test_validation_gemv_lists_fused(lib):
+    for key in ("tables", "entries", "eb", "cbs", "scales", "outs", "ys"):
+        assert lists_fused(**{key: None}) == binding.AQLM_ERR_NULL
+    assert lists_fused(n=0) == binding.AQLM_ERR_SHAPE
+    assert lists_fused(n=9) == binding.AQLM_ERR_SHAPE
+    assert lists_fused(tables=[A, 0]) == binding.AQLM_ERR_NULL
+    assert lists_fused(x=0) == binding.AQLM_ERR_NULL
+    assert lists_fused(ws=0) == binding.AQLM_ERR_NULL
+    assert lists_fused(M=2, B=8) == binding.AQLM_ERR_SCHEME
+    assert lists_fused(batch=2) == binding.AQLM_ERR_SHAPE
+    assert lists_fused(outs=[64, -1]) == binding.AQLM_ERR_SHAPE
+    assert lists_fused(eb=[1 << 20, -1]) == binding.AQLM_ERR_SHAPE
+    assert lists_fused(entries=[A, A + 4]) == binding.AQLM_ERR_ALIGN
+    assert lists_fused(ws=A + 8) == binding.AQLM_ERR_ALIGN
+    one = lists_geometry_sizes(64, 512)[1]
+    assert lists_fused(ws_bytes=2 * one - 1) == binding.AQLM_ERR_SHAPE          # 2 x 16 KB, 256-aligned
+    assert lists_fused(outs=[0, 0], tables=[0, 0], x=0, ws=0) == binding.AQLM_OK
+    assert lists_fused(batch=0, x=0, ws=0) == binding.AQLM_OK
+
+
+def test_lists_fused_workspace_bytes(lib):
+    one = lambda o, i: -(-lists_geometry_sizes(o, i)[1] // 256) * 256
+    assert binding.lists_fused_workspace_bytes([4096, 4096, 4096], 4096) == 3 * one(4096, 4096)
+    assert binding.lists_fused_workspace_bytes([11008, 0, 100], 4096) == one(11008, 4096) + one(100, 4096)
+    with pytest.raises(ValueError):
+        binding.lists_fused_workspace_bytes([], 4096)
+    with pytest.raises(ValueError):
+        binding.lists_fused_workspace_bytes([64], 4100)

@@ -182,3 +182,30 @@ def test_gemv_lists_empty_batch_and_layer():
     assert y.shape == (0, 64)
     z = E.aqlm_lists_pack(torch.zeros((0, 64, 1), dtype=torch.int16, device="cuda"))
     assert z.steps == 0 and z.table.numel() == 8
+
+
+@pytest.mark.parametrize("outs,n_in", [((4096, 4096, 4096), 4096), ((11008, 11008), 4096), ((300, 0, 65, 1), 9000),
+                                       ((1024, 8192), 8192)])
+def test_gemv_lists_fused_matches_separate_and_oracle(outs, n_in):
+    """One launch for layers that share x: bit-identical to separate calls; sampled rows against the oracle."""
+    x = synth.make_activations(n_in, 1, seed=11)
+    xd = torch.from_numpy(x).cuda()
+    layers, devs, hosts = [], [], []
+    for li, out in enumerate(outs):
+        L = synth.make_layer("1x16", out, n_in, seed=20 + li)
+        cb, s = torch.from_numpy(L.codebooks).cuda(), torch.from_numpy(L.scales).cuda()
+        lists = E.aqlm_lists_pack(torch.from_numpy(L.codes).cuda())
+        layers.append((lists, cb, s))
+        hosts.append(L)
+    ys = E.aqlm_linear_gemv_lists_fused(layers, xd)
+    torch.cuda.synchronize()
+    for (lists, cb, s), y, L in zip(layers, ys, hosts):
+        if L.out_features == 0:
+            assert y.shape == (1, 0)
+            continue
+        y_sep = E.aqlm_linear_gemv_lists(lists, cb, s, xd)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_sep.view(torch.int16))
+        rows = sample_rows(L.out_features, 48)
+        got = y.cpu().numpy().astype(np.float64)[:, rows]
+        assert_close(got, O.linear_ref_rows_f64(L.codes, L.codebooks, L.scales, x, rows), f"fused {outs}")
