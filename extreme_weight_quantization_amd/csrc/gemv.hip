@@ -99,22 +99,11 @@ __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restr
     return acc;
 }
 
+// The product for one layer, run by workgroup bid of the nwg that serve it.
 template <int SCHEME, int REPL, bool VEC, int RTP>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvLayers L,
-                                                            const f16* __restrict__ x,
-                                                            int in, int T) {
-    // This workgroup's layer: the number of layer ends at or below blockIdx.x.
-    int li = 0;
-#pragma unroll
-    for (int i = 0; i + 1 < kGemvMaxLayers; ++i) li += (i + 1 < L.n && (int)blockIdx.x >= L.wg_end[i]) ? 1 : 0;
-    const int wg0 = li > 0 ? L.wg_end[li > 0 ? li - 1 : 0] : 0;
-    const int bid = (int)blockIdx.x - wg0;     // workgroup index within the layer
-    const int nwg = L.wg_end[li] - wg0;        // workgroups of the layer
-    const uint8_t* __restrict__ codes = static_cast<const uint8_t*>(L.codes[li]);
-    const f16* __restrict__ codebooks = static_cast<const f16*>(L.codebooks[li]);
-    const f16* __restrict__ scales = static_cast<const f16*>(L.scales[li]);
-    f16* __restrict__ y = static_cast<f16*>(L.y[li]);
-    const int out = L.out[li];
+__device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, const f16* __restrict__ codebooks,
+                                          const f16* __restrict__ scales, f16* __restrict__ y, const int out,
+                                          const int bid, const int nwg, const f16* __restrict__ x, int in, int T) {
 
     extern __shared__ u32x4 smem[];
     constexpr int kCbSlots = (SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0;
@@ -245,18 +234,54 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvLayers L,
     if ((warm[0] ^ warm[3]) == 0x9e3779b9u && tid == 0xffff) y[0] = (f16)0.f;
 }
 
+// One layer: its arguments directly (a small argument block, read in one round trip).
+template <int SCHEME, int REPL, bool VEC, int RTP>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __restrict__ codes,
+                                                            const f16* __restrict__ codebooks,
+                                                            const f16* __restrict__ scales, f16* __restrict__ y,
+                                                            int out, const f16* __restrict__ x, int in, int T) {
+    gemv_body<SCHEME, REPL, VEC, RTP>(codes, codebooks, scales, y, out, (int)blockIdx.x, (int)gridDim.x, x, in, T);
+}
+
+// Several layers that share x: the workgroup's layer is the number of layer ends at
+// or below blockIdx.x; its first and last workgroups are picked from the ends
+// already in scalar registers.
+template <int SCHEME, int REPL, bool VEC, int RTP>
+__global__ __launch_bounds__(kGemvThreads) void gemv_fused_kernel(const GemvLayers L, const f16* __restrict__ x,
+                                                                  int in, int T) {
+    int li = 0, wg0 = 0, wg1 = L.wg_end[0];
+#pragma unroll
+    for (int i = 0; i + 1 < kGemvMaxLayers; ++i) {
+        const bool past = i + 1 < L.n && (int)blockIdx.x >= L.wg_end[i];
+        li += past ? 1 : 0;
+        wg0 = past ? L.wg_end[i] : wg0;
+        wg1 = past ? L.wg_end[i + 1] : wg1;
+    }
+    gemv_body<SCHEME, REPL, VEC, RTP>(static_cast<const uint8_t*>(L.codes[li]),
+                                      static_cast<const f16*>(L.codebooks[li]),
+                                      static_cast<const f16*>(L.scales[li]), static_cast<f16*>(L.y[li]), L.out[li],
+                                      (int)blockIdx.x - wg0, wg1 - wg0, x, in, T);
+}
+
 template <int SCHEME, int REPL, bool VEC, int RTP>
 static hipError_t launch_gemv_t(const GemvLayers& layers, const void* x, int in, int T, hipStream_t stream) {
-    auto kern = gemv_kernel<SCHEME, REPL, VEC, RTP>;
+    const bool fused = layers.n > 1;
+    const void* kern = fused ? (const void*)gemv_fused_kernel<SCHEME, REPL, VEC, RTP>
+                             : (const void*)gemv_kernel<SCHEME, REPL, VEC, RTP>;
     const size_t lds = (size_t)((SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0) * 16 +
                        (size_t)kGemvWaves * kRedFloats * sizeof(float);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(layers.wg_end[layers.n - 1]), dim3(kGemvThreads), lds, stream,
-                       layers, (const f16*)x, in, T);
+    if (fused)
+        hipLaunchKernelGGL((gemv_fused_kernel<SCHEME, REPL, VEC, RTP>), dim3(layers.wg_end[layers.n - 1]),
+                           dim3(kGemvThreads), lds, stream, layers, (const f16*)x, in, T);
+    else
+        hipLaunchKernelGGL((gemv_kernel<SCHEME, REPL, VEC, RTP>), dim3(layers.wg_end[0]), dim3(kGemvThreads), lds,
+                           stream, static_cast<const uint8_t*>(layers.codes[0]),
+                           static_cast<const f16*>(layers.codebooks[0]), static_cast<const f16*>(layers.scales[0]),
+                           static_cast<f16*>(layers.y[0]), layers.out[0], (const f16*)x, in, T);
     return hipGetLastError();
 }
 
