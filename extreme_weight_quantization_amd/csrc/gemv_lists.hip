@@ -49,7 +49,8 @@ constexpr int kSliceBits = 13;
 constexpr int kSliceWords = 1 << kSliceBits;     // codewords per slice: 128 KB of LDS
 constexpr int kListThreads = 1024;
 constexpr int kListWaves = kListThreads / kWave;
-constexpr int kListRing = 8;                     // entry loads in flight per lane
+constexpr int kListRing = 8;                     // entry loads per lane and chunk of steps
+constexpr int kListLongPart = 64;                // launches whose parts have this many steps use two rings
 constexpr int kWgPerSlice = 32;                  // workgroups per (slice, block): 256 in all
 constexpr int kReduceParts = 4;                  // threads per row in the partial sum
 
@@ -172,7 +173,9 @@ __device__ __forceinline__ int layer_of(const int* end, int n, int b, int* base)
     return l;
 }
 
-// ---- the product: workgroup bid of one layer
+// ---- the product: workgroup bid of one layer.  LONG: the parts have many steps (two
+// rings of entries in flight); otherwise one ring and a barrier that waits for the fill only.
+template <bool LONG>
 __device__ __forceinline__ void lists_product(const uint32_t* __restrict__ table, const uint32_t* __restrict__ entries,
                                               uint64_t cap_steps, const f16* __restrict__ codebook,
                                               const f16* __restrict__ x, float* __restrict__ partial,
@@ -181,13 +184,113 @@ __device__ __forceinline__ void lists_product(const uint32_t* __restrict__ table
     u32x4* cbs = smem;                 // the slice: kSliceWords codewords
     u32x4* xs = smem + kSliceWords;    // the x block: Z + 1 chunks of 8 fp16, chunk Z = 0
     float* red = reinterpret_cast<float*>(xs + geo.Z + 1);   // P > 1: the R * P unit sums, 64 per unit
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the table reads are scalar loads
     // workgroup -> (slice, block, index among the workgroups of the pair); consecutive
     // workgroups go to different XCDs, so the workgroups of an XCD share one slice in its L2
     const int s = bid % kSlices;
     const int rest = bid / kSlices;
     const int k = rest % geo.J, wi = rest / geo.J;
     const int out_pad = geo.n_rt * 64;
+
+    // units (r, p) of this workgroup: its r-th row tile, p-th of P equal parts of the steps
+    const int n_units = geo.R * geo.P;
+    struct Work {
+        const uint32_t* e;   // this lane's column of the unit's entries
+        int t0, n, rt;       // first step, steps, row tile (rt < 0: no unit)
+    };
+    auto work_of = [&](int uu) -> Work {
+        Work w{entries, 0, 0, -1};
+        if (uu >= n_units) return w;
+        const int r = uu / geo.P, p = uu % geo.P;
+        const int rt = wi + r * geo.W;
+        if (rt >= geo.n_rt) return w;
+        const int64_t unit = ((int64_t)s * geo.J + k) * geo.n_rt + rt;
+        const uint64_t off = table[2 * unit];
+        uint64_t L = table[2 * unit + 1];
+        if (off + L > cap_steps) L = 0;   // a table that does not fit the entries reads nothing
+        w.t0 = (int)((uint64_t)p * L / geo.P);
+        w.n = (int)((uint64_t)(p + 1) * L / geo.P) - w.t0;
+        w.e = entries + off * 64 + lane;
+        w.rt = rt;
+        return w;
+    };
+    // step t of a unit's part, clamped to its last step (prefetches past the end reread it)
+    auto fetch = [&](const Work& w, int t) -> uint32_t { return w.e[(size_t)(w.t0 + min(t, w.n - 1)) * 64]; };
+    auto lookup = [&](uint32_t en, float acc) {
+        return dot8(cbs[en & (kSliceWords - 1)], xs[min((int)(en >> kSliceBits), geo.Z)], acc);
+    };
+    auto finish = [&](const Work& w, int uu, float acc) {
+        if (geo.P > 1)
+            red[uu * 64 + lane] = acc;
+        else
+            partial[(size_t)(s * geo.J + k) * out_pad + w.rt * 64 + lane] = acc;
+    };
+    uint32_t ra[kListRing] = {}, rb[kListRing] = {};
+    // Short parts: one ring of kListRing entries, refilled a chunk ahead.  Every chunk
+    // issues its 2 kListRing LDS reads before the first product.
+    auto run_short = [&](const Work& w, int uu) {
+        float acc = 0.f;
+        int base = 0;
+        for (; base + kListRing <= w.n; base += kListRing) {
+            u32x4 wv[kListRing], xv[kListRing];
+#pragma unroll
+            for (int i = 0; i < kListRing; ++i) {
+                const uint32_t en = ra[i];
+                ra[i] = fetch(w, base + i + kListRing);
+                wv[i] = cbs[en & (kSliceWords - 1)];
+                xv[i] = xs[min((int)(en >> kSliceBits), geo.Z)];
+            }
+#pragma unroll
+            for (int i = 0; i < kListRing; ++i) acc = dot8(wv[i], xv[i], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < kListRing; ++i)   // the last n % kListRing steps, in order
+            if (base + i < w.n) acc = lookup(ra[i], acc);
+        finish(w, uu, acc);
+    };
+    // Long parts: two rings; chunk c is consumed from ring c % 2 while the other ring is
+    // in flight, so a chunk waits only for loads issued a whole chunk earlier.
+    auto run_long = [&](const Work& w, int uu) {
+        float acc = 0.f;
+        auto chunk = [&](uint32_t(&r)[kListRing], int next) {
+            u32x4 wv[kListRing], xv[kListRing];
+#pragma unroll
+            for (int i = 0; i < kListRing; ++i) {
+                wv[i] = cbs[r[i] & (kSliceWords - 1)];
+                xv[i] = xs[min((int)(r[i] >> kSliceBits), geo.Z)];
+            }
+#pragma unroll
+            for (int i = 0; i < kListRing; ++i) r[i] = fetch(w, next + i);
+#pragma unroll
+            for (int i = 0; i < kListRing; ++i) acc = dot8(wv[i], xv[i], acc);
+        };
+        int base = 0;
+        for (; base + 2 * kListRing <= w.n; base += 2 * kListRing) {
+            chunk(ra, base + 2 * kListRing);
+            __builtin_amdgcn_sched_barrier(0);   // keep ring a's refill ahead of ring b's reads
+            chunk(rb, base + 3 * kListRing);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < kListRing; ++i)   // the last n % (2 kListRing) steps, in order
+            if (base + i < w.n) acc = lookup(ra[i], acc);
+#pragma unroll
+        for (int i = 0; i < kListRing; ++i)
+            if (base + kListRing + i < w.n) acc = lookup(rb[i], acc);
+        finish(w, uu, acc);
+    };
+    auto prefetch_long = [&](const Work& w) {
+#pragma unroll
+        for (int i = 0; i < kListRing; ++i) ra[i] = fetch(w, i);
+#pragma unroll
+        for (int i = 0; i < kListRing; ++i) rb[i] = fetch(w, kListRing + i);
+    };
+
+    // the wave's first unit: its table entry (a scalar load) is read before the LDS fill,
+    // and its first entries are requested right after the fill, so that they arrive while
+    // the fill is in flight without delaying it
+    const Work first = work_of(wave);
 
     // slice and x block into LDS (lane l of a wave writes 16 bytes at base + 16 l)
     {
@@ -204,59 +307,34 @@ __device__ __forceinline__ void lists_product(const uint32_t* __restrict__ table
                                              0);
         if (tid == 0) xs[geo.Z] = u32x4{0u, 0u, 0u, 0u};
     }
-
-    // units (r, p) of this workgroup: its r-th row tile, p-th of P equal parts of the steps
-    const int n_units = geo.R * geo.P;
-    bool waited = false;
-    for (int uu = wave; uu < n_units; uu += kListWaves) {
-        const int r = uu / geo.P, p = uu % geo.P;
-        const int rt = wi + r * geo.W;
-        if (rt >= geo.n_rt) break;
-        const int64_t unit = ((int64_t)s * geo.J + k) * geo.n_rt + rt;
-        const uint64_t off = table[2 * unit];
-        uint64_t L = table[2 * unit + 1];
-        if (off + L > cap_steps) L = 0;   // a table that does not fit the entries reads nothing
-        const int t0 = (int)((uint64_t)p * L / geo.P), t1 = (int)((uint64_t)(p + 1) * L / geo.P);
-        const int n = t1 - t0;
-        const uint32_t* e = entries + off * 64 + lane;
-        auto fetch = [&](int t) -> uint32_t { return e[(size_t)min(t0 + t, t1 - 1) * 64]; };
-        uint32_t ring[kListRing] = {};
-        if (n > 0) {
-#pragma unroll
-            for (int i = 0; i < kListRing; ++i) ring[i] = fetch(i);
+    if constexpr (LONG) {
+        if (first.n > 0) prefetch_long(first);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (first.rt >= 0) run_long(first, wave);
+        for (int uu = wave + kListWaves; uu < n_units; uu += kListWaves) {   // only when R > 16 (then P = 1)
+            const Work w = work_of(uu);
+            if (w.rt < 0) break;
+            if (w.n > 0) prefetch_long(w);
+            run_long(w, uu);
         }
-        if (!waited) {   // the LDS fill (issued before the ring) has landed in every wave
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            waited = true;
-        }
-        float acc = 0.f;
-        int base = 0;
-        // whole chunks: all 2 * kListRing LDS reads are in flight before the first product
-        for (; base + kListRing <= n; base += kListRing) {
-            u32x4 w[kListRing], xv[kListRing];
+    } else {
+        // Exactly kListRing loads follow the fill (the table's first word stands in when the
+        // wave has no steps): once at most kListRing loads are pending, this wave's part of
+        // the fill has landed (loads complete in order).
+        const bool any = first.n > 0;
 #pragma unroll
-            for (int i = 0; i < kListRing; ++i) {
-                const uint32_t en = ring[i];
-                ring[i] = fetch(base + i + kListRing);   // clamped to the unit's last step
-                w[i] = cbs[en & (kSliceWords - 1)];
-                xv[i] = xs[min((int)(en >> kSliceBits), geo.Z)];
+        for (int i = 0; i < kListRing; ++i) ra[i] = any ? fetch(first, i) : table[0];
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kListRing) : "memory");
+        if (first.rt >= 0) run_short(first, wave);
+        for (int uu = wave + kListWaves; uu < n_units; uu += kListWaves) {
+            const Work w = work_of(uu);
+            if (w.rt < 0) break;
+            if (w.n > 0) {
+#pragma unroll
+                for (int i = 0; i < kListRing; ++i) ra[i] = fetch(w, i);
             }
-#pragma unroll
-            for (int i = 0; i < kListRing; ++i) acc = dot8(w[i], xv[i], acc);
+            run_short(w, uu);
         }
-#pragma unroll
-        for (int i = 0; i < kListRing; ++i)   // the last n % kListRing steps, in order
-            if (base + i < n)
-                acc = dot8(cbs[ring[i] & (kSliceWords - 1)], xs[min((int)(ring[i] >> kSliceBits), geo.Z)], acc);
-        if (geo.P > 1)
-            red[uu * 64 + lane] = acc;
-        else
-            partial[(size_t)(s * geo.J + k) * out_pad + rt * 64 + lane] = acc;
-    }
-    if (!waited) {   // no unit: the barrier is still everyone's
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
     }
     if (geo.P > 1) {   // R * P <= 16: each wave had at most one unit; wave r adds the P parts of row tile r
         __syncthreads();
@@ -270,20 +348,22 @@ __device__ __forceinline__ void lists_product(const uint32_t* __restrict__ table
 }
 
 // A single layer: its arguments directly (one small argument block).
+template <bool LONG>
 __global__ __launch_bounds__(kListThreads) void gemv_lists_kernel(const uint32_t* __restrict__ table,
                                                                   const uint32_t* __restrict__ entries,
                                                                   uint64_t cap_steps, const f16* __restrict__ codebook,
                                                                   const f16* __restrict__ x,
                                                                   float* __restrict__ partial, ListsGeo geo) {
-    lists_product(table, entries, cap_steps, codebook, x, partial, geo, blockIdx.x);
+    lists_product<LONG>(table, entries, cap_steps, codebook, x, partial, geo, blockIdx.x);
 }
 
 // Several layers that share x: the workgroup's layer from the table.
+template <bool LONG>
 __global__ __launch_bounds__(kListThreads) void gemv_lists_fused_kernel(const ListsLayers L,
                                                                         const f16* __restrict__ x) {
     int first = 0;
     const int l = layer_of(L.wg_end, L.n, blockIdx.x, &first);
-    lists_product(L.table[l], L.entries[l], L.cap[l], static_cast<const f16*>(L.codebook[l]), x, L.partial[l],
+    lists_product<LONG>(L.table[l], L.entries[l], L.cap[l], static_cast<const f16*>(L.codebook[l]), x, L.partial[l],
                   L.geo[l], blockIdx.x - first);
 }
 
@@ -396,16 +476,22 @@ hipError_t launch_gemv_lists_fused(ListsLayers L, const void* x, int64_t in, hip
         L.blk_end[l] = (int)blks;
     }
     const bool multi = L.n > 1;
-    const void* kern = multi ? (const void*)gemv_lists_fused_kernel : (const void*)gemv_lists_kernel;
+    // long parts: about Gb/8 steps per row tile (uniform codes) split over P waves
+    bool long_parts = true;
+    for (int l = 0; l < L.n; ++l) long_parts &= L.geo[l].Gb / 8 / L.geo[l].P >= kListLongPart;
+    const void* kern = multi ? (long_parts ? (const void*)gemv_lists_fused_kernel<true>
+                                           : (const void*)gemv_lists_fused_kernel<false>)
+                             : (long_parts ? (const void*)gemv_lists_kernel<true> : (const void*)gemv_lists_kernel<false>);
     const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if (multi) {
-        hipLaunchKernelGGL(gemv_lists_fused_kernel, dim3((unsigned)wgs), dim3(kListThreads), lds, stream, L,
-                           static_cast<const f16*>(x));
+        auto fk = long_parts ? gemv_lists_fused_kernel<true> : gemv_lists_fused_kernel<false>;
+        hipLaunchKernelGGL(fk, dim3((unsigned)wgs), dim3(kListThreads), lds, stream, L, static_cast<const f16*>(x));
         hipLaunchKernelGGL(lists_reduce_fused_kernel, dim3((unsigned)blks), dim3(64 * kReduceParts), 0, stream, L);
     } else {   // one layer: the compact argument lists
         const ListsGeo& g = L.geo[0];
-        hipLaunchKernelGGL(gemv_lists_kernel, dim3((unsigned)wgs), dim3(kListThreads), lds, stream, L.table[0],
+        auto sk = long_parts ? gemv_lists_kernel<true> : gemv_lists_kernel<false>;
+        hipLaunchKernelGGL(sk, dim3((unsigned)wgs), dim3(kListThreads), lds, stream, L.table[0],
                            L.entries[0], L.cap[0], static_cast<const f16*>(L.codebook[0]),
                            static_cast<const f16*>(x), L.partial[0], g);
         hipLaunchKernelGGL(lists_reduce_kernel, dim3((unsigned)blks), dim3(64 * kReduceParts), 0, stream,

@@ -96,6 +96,14 @@ def test_gemv_lists_basis_vectors_exact():
         np.testing.assert_array_equal(y[0], w16[:, col])
 
 
+def test_gemv_lists_long_parts_full():
+    """520 x 262144: 32 blocks of 1024 groups, one workgroup per (slice, block), 9 row tiles (the last
+    ragged), undivided parts of ~160 steps: the two-ring path, every output against the oracle."""
+    L = synth.make_layer("1x16", 520, 262144, seed=13)
+    y, _ = run(L)
+    assert_close(y, O.linear_ref_f64(L.codes, L.codebooks, L.scales, L.x), "520x262144")
+
+
 @pytest.mark.parametrize("shape", synth.LLAMA2_7B_SHAPES)
 def test_gemv_lists_7b(shape):
     out, n_in = shape
