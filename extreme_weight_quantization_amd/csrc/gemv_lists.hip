@@ -318,12 +318,15 @@ __device__ __forceinline__ void lists_product(const uint32_t* __restrict__ table
             run_long(w, uu);
         }
     } else {
-        // Exactly kListRing loads follow the fill (the table's first word stands in when the
-        // wave has no steps): once at most kListRing loads are pending, this wave's part of
-        // the fill has landed (loads complete in order).
+        // Exactly kListRing vector loads follow the fill: once at most kListRing loads are
+        // pending, this wave's part of the fill has landed (loads complete in order).  A wave
+        // without steps reads one of the table's first two words instead; both addresses
+        // depend on the lane, so neither can become a scalar load.
         const bool any = first.n > 0;
+        const uint32_t* stand_in = table + (lane & 1);
 #pragma unroll
-        for (int i = 0; i < kListRing; ++i) ra[i] = any ? fetch(first, i) : table[0];
+        for (int i = 0; i < kListRing; ++i)
+            ra[i] = *(any ? first.e + (size_t)(first.t0 + min(i, first.n - 1)) * 64 : stand_in);
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kListRing) : "memory");
         if (first.rt >= 0) run_short(first, wave);
         for (int uu = wave + kListWaves; uu < n_units; uu += kListWaves) {
