@@ -26,7 +26,7 @@ Sources (cited by page title and section):
   (1, 4), (2, 8), ..., (8, 32) all give 2 bits; a B that is not a multiple of
   8 leaves unused bits in the bytes that hold each code.
 
-Readings where the pages are silent (each one listed in the design doc):
+Readings where the pages are silent:
 
 * group j of row i covers columns [j*g, (j+1)*g); codes are stored
   ``[d_out][d_in/g][M]``; codebooks ``[M][2^B][g]``; scales ``[d_out]``;
@@ -220,8 +220,7 @@ def within_tolerance(y, y_ref):
 # procedure": per linear layer, the codes are learned first with the codebooks
 # fixed, and those codebooks are initialised with a residual k-means approach.
 # The learning loss itself did not survive text extraction and is weighted by
-# calibration activations, so these are the data-free readings, each listed in
-# the design doc:
+# calibration activations, so these are the data-free readings:
 #
 # * a group's target is its weights divided by the row's scale (scales are
 #   given; the pages do not say how they are initialised), in fp32;
