@@ -15,8 +15,13 @@
 //    waves of a workgroup take slabs round-robin, and for each slab keep the
 //    activation operand (x, batch padded to 16 columns) in registers while
 //    they run through the workgroup's row tiles;
-//  * lane l of a wave decodes group (slab, 8*(l/16) + q) of row l%16 for the
-//    q-th product, so one 16-byte code load per lane covers 8 products;
+//  * one 16-byte load gives lane l the codes of groups 8*(l/16) .. 8*(l/16)+7
+//    of its slab in row l%16.  Below batch 8, lane l decodes group
+//    8*(l/16) + q for the q-th product.  From batch 8 up, the four lanes of a
+//    row first transpose their 4-byte words (two cross-row lane swaps), after
+//    which lane l decodes group 8*(q/2) + 2*(l/16) + q%2: the k order inside
+//    each product changes, and the x pieces of one product then lie in one
+//    128-byte line per batch row instead of four;
 //  * the 2x8 codebooks live in LDS, replicated REPL times with entry k of
 //    replica r at 16-byte slot (2k + m) * REPL + r; lane l reads replica
 //    l % REPL, which spreads the 16 lanes served together over distinct bank
@@ -63,6 +68,24 @@ __device__ __forceinline__ u32x4 load_codes(const uint8_t* __restrict__ codes, i
     }
 }
 
+// The four 16-lane rows of a wave hold words 4k .. 4k+3 (row k) of a 16-word
+// slab row; afterwards row k holds words k, k+4, k+8, k+12.  Each swap
+// exchanges one register between two rows at the same lane position: first
+// rows {0,1} with {2,3}, then rows {0,2} with {1,3}.
+__device__ __forceinline__ u32x4 transpose_rows4(const u32x4 v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    return u32x4{c[0], c[1], d[0], d[1]};
+}
+
+// Group of product q (0..7) in the slab for the lane of k-quarter kq.
+template <bool XT>
+__device__ __forceinline__ int slab_group(int kq, int q) {
+    return XT ? 8 * (q >> 1) + 2 * kq + (q & 1) : 8 * kq + q;
+}
+
 // Decodes the 8 groups of a code chunk into matrix-core A operands (fp16) and
 // accumulates their products with the activation operands bx into acc.
 // Groups past the end of the row (ok mask bit clear) contribute zero.  The
@@ -100,7 +123,8 @@ __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restr
 }
 
 // The product for one layer, run by workgroup bid of the nwg that serve it.
-template <int SCHEME, int REPL, bool VEC, int RTP>
+// XT: the transposed k order (batch 8 and up).
+template <int SCHEME, int REPL, bool VEC, int RTP, bool XT>
 __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, const f16* __restrict__ codebooks,
                                           const f16* __restrict__ scales, f16* __restrict__ y, const int out,
                                           const int bid, const int nwg, const f16* __restrict__ x, int in, int T) {
@@ -134,10 +158,9 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
     }
     f16x8 bx[8];
     auto load_x = [&](int s) {
-        const int g0 = s * kSlabGroups + kq * 8;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int grp = g0 + q;
+            const int grp = s * kSlabGroups + slab_group<XT>(kq, q);
             bx[q] = (lrow < T && grp < G)
                         ? as_f16x8(load16(x + (size_t)lrow * in + (size_t)grp * kGroup))
                         : f16x8{};
@@ -182,10 +205,9 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
         for (int i = 0; i < RTP; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         for (int s = s0; s < n_slab; s += kGemvWaves) {
-            const int g0 = s * kSlabGroups + kq * 8;   // first group of this lane's chunk
             u32x4 ccur[RTP];
 #pragma unroll
-            for (int i = 0; i < RTP; ++i) ccur[i] = cnext[i];
+            for (int i = 0; i < RTP; ++i) ccur[i] = XT ? transpose_rows4(cnext[i]) : cnext[i];
             // Prefetch the codes of this wave's next slab (or of the next pass).
             {
                 int sn = s + kGemvWaves, rtn = rt0;
@@ -199,7 +221,10 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
                 }
             }
             if (s != s_loaded) { load_x(s); s_loaded = s; }
-            const uint32_t gmask = (G - g0 >= 8) ? 0xffu : (G > g0 ? (1u << (G - g0)) - 1u : 0u);
+            uint32_t gmask = 0u;   // bit q: the group of product q is inside the row
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                gmask |= (s * kSlabGroups + slab_group<XT>(kq, q) < G) ? (1u << q) : 0u;
 #pragma unroll
             for (int i = 0; i < RTP; ++i) {
                 const int rt = rt0 + i * nwg;
@@ -235,18 +260,18 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
 }
 
 // One layer: its arguments directly (a small argument block, read in one round trip).
-template <int SCHEME, int REPL, bool VEC, int RTP>
+template <int SCHEME, int REPL, bool VEC, int RTP, bool XT>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __restrict__ codes,
                                                             const f16* __restrict__ codebooks,
                                                             const f16* __restrict__ scales, f16* __restrict__ y,
                                                             int out, const f16* __restrict__ x, int in, int T) {
-    gemv_body<SCHEME, REPL, VEC, RTP>(codes, codebooks, scales, y, out, (int)blockIdx.x, (int)gridDim.x, x, in, T);
+    gemv_body<SCHEME, REPL, VEC, RTP, XT>(codes, codebooks, scales, y, out, (int)blockIdx.x, (int)gridDim.x, x, in, T);
 }
 
 // Several layers that share x: the workgroup's layer is the number of layer ends at
 // or below blockIdx.x; its first and last workgroups are picked from the ends
 // already in scalar registers.
-template <int SCHEME, int REPL, bool VEC, int RTP>
+template <int SCHEME, int REPL, bool VEC, int RTP, bool XT>
 __global__ __launch_bounds__(kGemvThreads) void gemv_fused_kernel(const GemvLayers L, const f16* __restrict__ x,
                                                                   int in, int T) {
     int li = 0, wg0 = 0, wg1 = L.wg_end[0];
@@ -257,17 +282,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_fused_kernel(const GemvLaye
         wg0 = past ? L.wg_end[i] : wg0;
         wg1 = past ? L.wg_end[i + 1] : wg1;
     }
-    gemv_body<SCHEME, REPL, VEC, RTP>(static_cast<const uint8_t*>(L.codes[li]),
+    gemv_body<SCHEME, REPL, VEC, RTP, XT>(static_cast<const uint8_t*>(L.codes[li]),
                                       static_cast<const f16*>(L.codebooks[li]),
                                       static_cast<const f16*>(L.scales[li]), static_cast<f16*>(L.y[li]), L.out[li],
                                       (int)blockIdx.x - wg0, wg1 - wg0, x, in, T);
 }
 
-template <int SCHEME, int REPL, bool VEC, int RTP>
+template <int SCHEME, int REPL, bool VEC, int RTP, bool XT>
 static hipError_t launch_gemv_t(const GemvLayers& layers, const void* x, int in, int T, hipStream_t stream) {
     const bool fused = layers.n > 1;
-    const void* kern = fused ? (const void*)gemv_fused_kernel<SCHEME, REPL, VEC, RTP>
-                             : (const void*)gemv_kernel<SCHEME, REPL, VEC, RTP>;
+    const void* kern = fused ? (const void*)gemv_fused_kernel<SCHEME, REPL, VEC, RTP, XT>
+                             : (const void*)gemv_kernel<SCHEME, REPL, VEC, RTP, XT>;
     const size_t lds = (size_t)((SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0) * 16 +
                        (size_t)kGemvWaves * kRedFloats * sizeof(float);
     if (lds > 65536) {
@@ -275,10 +300,10 @@ static hipError_t launch_gemv_t(const GemvLayers& layers, const void* x, int in,
         if (e != hipSuccess) return e;
     }
     if (fused)
-        hipLaunchKernelGGL((gemv_fused_kernel<SCHEME, REPL, VEC, RTP>), dim3(layers.wg_end[layers.n - 1]),
+        hipLaunchKernelGGL((gemv_fused_kernel<SCHEME, REPL, VEC, RTP, XT>), dim3(layers.wg_end[layers.n - 1]),
                            dim3(kGemvThreads), lds, stream, layers, (const f16*)x, in, T);
     else
-        hipLaunchKernelGGL((gemv_kernel<SCHEME, REPL, VEC, RTP>), dim3(layers.wg_end[0]), dim3(kGemvThreads), lds,
+        hipLaunchKernelGGL((gemv_kernel<SCHEME, REPL, VEC, RTP, XT>), dim3(layers.wg_end[0]), dim3(kGemvThreads), lds,
                            stream, static_cast<const uint8_t*>(layers.codes[0]),
                            static_cast<const f16*>(layers.codebooks[0]), static_cast<const f16*>(layers.scales[0]),
                            static_cast<f16*>(layers.y[0]), layers.out[0], (const f16*)x, in, T);
@@ -317,19 +342,28 @@ static void deal_workgroups(GemvLayers& layers, int cus) {
     }
 }
 
+// Below this batch the stored k order is kept; from it up the lanes transpose
+// their code words so that each x load touches one line per batch row.
+constexpr int kGemvTransposeBatch = 8;
+
+template <int SCHEME, int REPL, int RTP>
+static hipError_t launch_gemv_s(const GemvLayers& layers, const void* x, int n, int T, hipStream_t stream) {
+    const bool vec = (n % 64) == 0;   // 16-byte aligned code rows
+    if (T >= kGemvTransposeBatch)
+        return vec ? launch_gemv_t<SCHEME, REPL, true, RTP, true>(layers, x, n, T, stream)
+                   : launch_gemv_t<SCHEME, REPL, false, RTP, true>(layers, x, n, T, stream);
+    return vec ? launch_gemv_t<SCHEME, REPL, true, RTP, false>(layers, x, n, T, stream)
+               : launch_gemv_t<SCHEME, REPL, false, RTP, false>(layers, x, n, T, stream);
+}
+
 hipError_t launch_gemv_fused(int scheme, GemvLayers layers, const void* x, int64_t in,
                              int64_t batch, hipStream_t stream) {
     constexpr int RTP = 2;
     if (layers.n < 1) return hipSuccess;
     deal_workgroups(layers, device_cu_count());
-    const bool vec = (in % 64) == 0;   // 16-byte aligned code rows
     const int n = (int)in, T = (int)batch;
-    if (scheme == kScheme2x8) {
-        return vec ? launch_gemv_t<kScheme2x8, 16, true, RTP>(layers, x, n, T, stream)
-                   : launch_gemv_t<kScheme2x8, 16, false, RTP>(layers, x, n, T, stream);
-    }
-    return vec ? launch_gemv_t<kScheme1x16, 1, true, RTP>(layers, x, n, T, stream)
-               : launch_gemv_t<kScheme1x16, 1, false, RTP>(layers, x, n, T, stream);
+    if (scheme == kScheme2x8) return launch_gemv_s<kScheme2x8, 16, RTP>(layers, x, n, T, stream);
+    return launch_gemv_s<kScheme1x16, 1, RTP>(layers, x, n, T, stream);
 }
 
 hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, const void* scales,

@@ -140,6 +140,9 @@ def run_gemv(layer):
     (300, 2048, 7),
     (16, 16384, 2),     # wide row: many slabs per wave
     (4096 + 8, 256, 4), # many row tiles per workgroup
+    (100, 520, 12),     # batch 8 and up (transposed k order): ragged rows, unaligned code rows
+    (72, 4104, 8),      # the same at the threshold batch, a partial last slab
+    (33, 4160, 16),     # aligned code rows, partial last slab, ragged row tile
 ])
 def test_gemv_small(scheme, out, n_in, batch):
     L = synth.make_layer(scheme, out, n_in, batch=batch, seed=0)
@@ -175,10 +178,11 @@ def test_gemv_basis_vectors_exact(scheme):
     np.testing.assert_array_equal(y, w16[:, cols].T)
 
 
+@pytest.mark.parametrize("batch", [1, 16])
 @pytest.mark.parametrize("shape", synth.LLAMA2_7B_SHAPES)
-def test_gemv_7b_1x16(shape):
+def test_gemv_7b_1x16(shape, batch):
     out, n_in = shape
-    L = synth.make_layer("1x16", out, n_in, batch=1, seed=0)
+    L = synth.make_layer("1x16", out, n_in, batch=batch, seed=0)
     y = run_gemv(L)
     rows = sample_rows(out)
     assert_close(y[:, rows], O.linear_ref_rows_f64(L.codes, L.codebooks, L.scales, L.x, rows), str(shape))
