@@ -449,9 +449,23 @@ def main():
                 y = torch.empty((2048, out), dtype=torch.float16, device="cuda")
                 us = time_calls(torch, lambda i: E.aqlm_linear_gemm(codes, cb, s, x, y), 10, 2)
                 tf = 2.0 * 2048 * out * n_in / (us * 1e-6) / 1e12
+                # two passes: the weights decoded once into a workspace, then the dense product
+                M, B, g, _ = SCHEMES[scheme]
+                ws = torch.empty((E.gemm_dequant_workspace_bytes(M, B, g, out, n_in),), dtype=torch.uint8,
+                                 device="cuda")
+                us2 = time_calls(torch, lambda i: E.aqlm_linear_gemm_dequant(codes, cb, s, x, y, ws), 10, 2)
+                w16 = ws.view(torch.float16).view(out, n_in)
+                usd = time_calls(torch, lambda i: E.aqlm_linear_decode(codes, cb, s, w16), 10, 2)
+                tf2 = 2.0 * 2048 * out * n_in / (us2 * 1e-6) / 1e12
                 gm[f"{scheme}_{out}x{n_in}"] = {"us": round(us, 1), "TFLOPs": round(tf, 1),
-                                                "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
-                del codes, s, x, y
+                                                "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                                "two_pass_us": round(us2, 1),
+                                                "two_pass_frac_mfma_peak": round(tf2 / MFMA_F16_PEAK_TFLOPS, 4),
+                                                "two_pass_decode_us": round(usd, 1),
+                                                "dense_product_frac_mfma_peak": round(
+                                                    2.0 * 2048 * out * n_in / ((us2 - usd) * 1e-6) / 1e12
+                                                    / MFMA_F16_PEAK_TFLOPS, 4)}
+                del codes, s, x, y, ws, w16
             torch.cuda.empty_cache()
         breakdown["gemm_prefill_2048"] = gm
         # standalone decode, 4096x4096

@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     aqlm_lists_pack,
     aqlm_linear_decode,
     aqlm_linear_gemm,
+    aqlm_linear_gemm_dequant,
+    gemm_dequant_workspace_bytes,
     aqlm_linear_gemv,
     aqlm_linear_gemv_fused,
     aqlm_encode_greedy,

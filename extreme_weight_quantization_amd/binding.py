@@ -21,6 +21,7 @@ EXPORTED = ("aqlm_linear_gemv", "aqlm_linear_gemv_fused", "aqlm_linear_gemm", "a
             "aqlm_encode_greedy", "aqlm_kmeans_workspace_bytes", "aqlm_kmeans_init",
             "aqlm_lists_table_bytes", "aqlm_lists_workspace_bytes", "aqlm_lists_plan", "aqlm_lists_fill",
             "aqlm_linear_gemv_lists", "aqlm_linear_gemv_lists_fused", "aqlm_lists_fused_workspace_bytes",
+            "aqlm_linear_gemm_dequant", "aqlm_gemm_dequant_workspace_bytes",
             "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
 FUSED_MAX_LAYERS = 8   # AQLM_FUSED_MAX_LAYERS
 
@@ -74,6 +75,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.aqlm_lists_fused_workspace_bytes.argtypes = [ci, ctypes.POINTER(i64), ci, ci, ci, i64,
                                                          ctypes.POINTER(i64)]
         lib.aqlm_lists_fused_workspace_bytes.restype = ci
+        lib.aqlm_linear_gemm_dequant.argtypes = [vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, i64, i64, i64, vp]
+        lib.aqlm_linear_gemm_dequant.restype = ci
+        lib.aqlm_gemm_dequant_workspace_bytes.argtypes = [ci, ci, ci, i64, i64, ctypes.POINTER(i64)]
+        lib.aqlm_gemm_dequant_workspace_bytes.restype = ci
         lib.aqlm_status_str.argtypes = [ci]
         lib.aqlm_status_str.restype = ctypes.c_char_p
         lib.aqlm_last_hip_error.argtypes = []
@@ -209,6 +214,37 @@ def aqlm_linear_gemv_fused(layers, x, ys=None):
 def aqlm_linear_gemm(codes, codebooks, scales, x, y=None):
     """Y = X W^T for a prefill batch of tokens (see aqlm.h)."""
     return _linear("aqlm_linear_gemm", codes, codebooks, scales, x, y)
+
+
+def gemm_dequant_workspace_bytes(M: int, B: int, g: int, out: int, n_in: int) -> int:
+    """Bytes of workspace aqlm_linear_gemm_dequant needs (the decoded weights; 0 when in % 64 != 0)."""
+    n = ctypes.c_int64(0)
+    _check(load_library().aqlm_gemm_dequant_workspace_bytes(M, B, g, out, n_in, ctypes.byref(n)))
+    return int(n.value)
+
+
+def aqlm_linear_gemm_dequant(codes, codebooks, scales, x, y=None, workspace=None):
+    """Y = X W^T in two passes: W decoded once into the workspace, then a dense fp16 product (see aqlm.h)."""
+    _check_tensors(codes, codebooks, scales, x)
+    M, B, g = _scheme(codes, codebooks)
+    out, G = int(codes.shape[0]), int(codes.shape[1])
+    n_in = G * g
+    if x.dim() != 2 or x.shape[1] != n_in:
+        raise ValueError(f"x must be [batch][{n_in}]")
+    batch = int(x.shape[0])
+    if y is None:
+        y = torch.empty((batch, out), dtype=torch.float16, device=x.device)
+    elif y.shape != (batch, out) or y.dtype != torch.float16 or not y.is_contiguous():
+        raise ValueError(f"y must be a contiguous float16 [{batch}][{out}] tensor")
+    need = gemm_dequant_workspace_bytes(M, B, g, out, n_in)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    _check(load_library().aqlm_linear_gemm_dequant(_ptr(codes), _ptr(codebooks), _ptr(scales), _ptr(x), _ptr(y),
+                                                   _ptr(workspace), workspace.numel(), M, B, g, out, n_in, batch,
+                                                   _stream(x.device)))
+    return y
 
 
 def aqlm_linear_decode(codes, codebooks, scales, w=None):

@@ -13,7 +13,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libaqlm.so")
-SOURCES = ["aqlm_api.hip", "decode.hip", "gemv.hip", "gemm.hip", "gemm_pipe.hip", "generic.hip", "encode.hip", "gemv_lists.hip"]
+SOURCES = ["aqlm_api.hip", "decode.hip", "gemv.hip", "gemm.hip", "gemm_pipe.hip", "generic.hip", "encode.hip", "gemv_lists.hip", "gemm_dense.hip"]
 ARCH = "gfx950"
 
 # No fast-math and no flush-to-zero: decode must be bit-exact.  Packed fp32

@@ -146,6 +146,39 @@ int aqlm_linear_gemm(const void* codes, const void* codebooks, const void* scale
                               (hipStream_t)stream));
 }
 
+int aqlm_gemm_dequant_workspace_bytes(int M, int B, int g, int64_t out, int64_t in, int64_t* bytes) {
+    if (!bytes) return AQLM_ERR_NULL;
+    if (!(M == 1 && B == 16 && g == 8) && !(M == 2 && B == 8 && g == 8) && !generic_scheme_ok(M, B, g))
+        return AQLM_ERR_SCHEME;
+    if (out < 0 || in < 1 || in > AQLM_MAX_IN || (in % g) != 0 || out > (int64_t)INT32_MAX - 16)
+        return AQLM_ERR_SHAPE;
+    *bytes = (in % 64 == 0) ? out * in * 2 : 0;
+    return AQLM_OK;
+}
+
+int aqlm_linear_gemm_dequant(const void* codes, const void* codebooks, const void* scales, const void* x,
+                             void* y, void* workspace, int64_t workspace_bytes, int M, int B, int g, int64_t out,
+                             int64_t in, int64_t batch, void* stream) {
+    int scheme = 0;
+    bool empty = false;
+    const int st = validate(Op::kGemm, codes, codebooks, scales, x, y, M, B, g, out, in, batch, &scheme, &empty);
+    if (st != AQLM_OK) return st;
+    if ((uint64_t)out * (uint64_t)(in / g) > (uint64_t)UINT32_MAX) return AQLM_ERR_SHAPE;
+    if (empty) return AQLM_OK;
+    if (in % 64 != 0)
+        return aqlm_linear_gemm(codes, codebooks, scales, x, y, M, B, g, out, in, batch, stream);
+    if (!workspace) return AQLM_ERR_NULL;
+    if (!aligned(workspace, 16)) return AQLM_ERR_ALIGN;
+    if (workspace_bytes < out * in * 2) return AQLM_ERR_SHAPE;
+    const hipStream_t s = (hipStream_t)stream;
+    const int dst = (scheme == kSchemeGeneric)
+                        ? finish(launch_decode_generic(GenericScheme{M, B, g}, codes, codebooks, scales, workspace,
+                                                       out, in, s))
+                        : finish(launch_decode(scheme, codes, codebooks, scales, workspace, out, in, s));
+    if (dst != AQLM_OK) return dst;
+    return finish(launch_gemm_dense(x, workspace, y, out, in, batch, s));
+}
+
 int aqlm_linear_decode(const void* codes, const void* codebooks, const void* scales, const void* x,
                        void* y, int M, int B, int g, int64_t out, int64_t in, int64_t batch,
                        void* stream) {

@@ -1,0 +1,215 @@
+// Prefill product on decoded weights:  Y[t][i] = sum_k X[t][k] W16[i][k].
+//
+// "The AQLM Quantization Algorithm, Explained", Figure 2 of the MCQ section:
+// at inference the product with the activations runs on dequantized
+// half-precision weights, each the sum of the selected codewords times the
+// row scale.  The two-pass prefill path first writes those weights once
+// (decode_kernel, bit-exact fp16, the scale already applied) and then runs
+// this dense fp16 matrix-core product over them.  Against the fused kernels,
+// which decode every W tile again for each 256-token tile, it trades 2 bytes
+// per weight of HBM traffic (written once, read once per XCD) for decoding
+// each weight once.
+//
+// A workgroup owns a 256-token x 128-row output tile and walks k in steps of
+// 64 inputs, each split into two k-halves of 32.  Eight waves each own a
+// 64x64 piece: they copy their share of the X and W halves straight from
+// global memory into LDS (direct-to-LDS loads), read 16-byte fragments and
+// run 16x16x32 fp16 matrix-core products with fp32 accumulators.
+//
+// Pipeline (one barrier per step; B_k is the barrier that ends step k):
+//   step k : load X and W of step k+3 half 0 and of step k+2 half 1;
+//            read half 1 of step k, multiply half 0 of step k;
+//            read half 0 of step k+1, multiply half 1 of step k;
+//            B_k waits for every load issued before step k.
+// X and W keep three stages each: 96 + 48 = 144 KB of LDS.
+//
+// LDS layout of one k-half of a tile: row r holds 4 chunks of 16 bytes; chunk c
+// sits in slot 4r + (c ^ ((r >> 2) & 3)).  A direct-to-LDS load writes 64
+// consecutive slots (16 whole rows), and the 16 lanes of a fragment read hit
+// 16 distinct bank groups.
+//
+// Tile order: consecutive workgroups go to different XCDs, so workgroup b
+// takes tile (b % 8) * per + b / 8 of the token-fastest tile order.  Each XCD
+// then holds a contiguous run of row tiles with all their token tiles: its L2
+// keeps its own W tiles, and the X tiles that its concurrent workgroups share.
+#include "aqlm_device.h"
+#include "aqlm_launch.h"
+
+namespace aqlm {
+
+namespace {
+
+constexpr int kDenseBM = 256;                // tokens per tile
+constexpr int kDenseBN = 128;                // output rows per tile
+constexpr int kDenseWaves = 8;
+constexpr int kDenseThreads = 64 * kDenseWaves;
+constexpr int kDenseXHalf = kDenseBM * 4;    // 16-byte slots of one X k-half
+constexpr int kDenseWHalf = kDenseBN * 4;    // 16-byte slots of one W k-half
+constexpr int kDenseStages = 3;
+constexpr int kDenseWOff = kDenseStages * 2 * kDenseXHalf;
+constexpr size_t kDenseLds = (size_t)(kDenseWOff + kDenseStages * 2 * kDenseWHalf) * 16;
+static_assert(kDenseLds <= 163840, "LDS budget");
+constexpr int kXcds = 8;                     // tile order only; any count gives correct results
+
+// s_waitcnt vmcnt(n) lgkmcnt(0), export counter at its maximum (n < 16).  The
+// builtin, unlike inline assembly, is seen by the compiler's own wait placement.
+constexpr int wait_vm_lgkm0(int n) { return n | (7 << 4); }
+// s_waitcnt lgkmcnt(0) with the vector-memory and export counters at their maxima
+constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
+// loads a wave issues per step: X 2 per half, W 1 per half
+constexpr int kDenseLoadsPerStep = 6;
+
+__device__ __forceinline__ int half_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
+    return (__attribute__((address_space(3))) void*)p;
+}
+
+// B_k: every load issued before this step has landed (this step's own stay in
+// flight), every LDS read of the workgroup is done.
+__device__ __forceinline__ void step_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kDenseLoadsPerStep));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __restrict__ x,
+                                                                   const f16* __restrict__ w, f16* __restrict__ y,
+                                                                   int out, int in, int T, int n_tt, int n_tiles,
+                                                                   int per_xcd) {
+    extern __shared__ u32x4 smem[];
+    u32x4* Xs = smem;                 // [stage 3][half 2][kDenseXHalf]
+    u32x4* Ws = smem + kDenseWOff;    // [stage 3][half 2][kDenseWHalf]
+    const int tile = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (tile >= n_tiles) return;      // the whole workgroup: the grid is rounded up to kXcds * per_xcd
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = (tile / n_tt) * kDenseBN;
+    const int t0 = (tile % n_tt) * kDenseBM;
+    const int n_k = in / 64;          // the launcher guarantees in % 64 == 0
+
+    // Half h of step j into stage j % 3.  Lane l of a 16-row load writes slot
+    // 64 q + l = 4 rr + (l & 3), which holds chunk c of row rr.
+    const int rr0 = lane >> 2;
+    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    auto load_x = [&](int j, int h) {
+        const int jc = min(j, n_k - 1);
+        u32x4* dst = Xs + ((j % kDenseStages) * 2 + h) * kDenseXHalf;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = 2 * wave + i;
+            const int tok = min(t0 + 16 * q + rr0, T - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)tok * in + (size_t)(8 * jc + 4 * h + c) * kGroup),
+                                             lds_ptr(dst + 64 * q), 16, 0, 0);
+        }
+    };
+    auto load_w = [&](int j, int h) {
+        const int jc = min(j, n_k - 1);
+        u32x4* dst = Ws + ((j % kDenseStages) * 2 + h) * kDenseWHalf;
+        const int row = min(n0 + 16 * wave + rr0, out - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(w + (size_t)row * in + (size_t)(8 * jc + 4 * h + c) * kGroup),
+                                         lds_ptr(dst + 64 * wave), 16, 0, 0);
+    };
+
+    const int wm = wave >> 1, wn = wave & 1;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fragments of half h of step j: lane l holds A[l%16][8(l/16)..] and B[8(l/16)..][l%16]
+    auto read_frags = [&](int j, int h, f16x8 (&a)[4], f16x8 (&b)[4]) {
+        const u32x4* xb = Xs + ((j % kDenseStages) * 2 + h) * kDenseXHalf;
+        const u32x4* wb = Ws + ((j % kDenseStages) * 2 + h) * kDenseWHalf;
+        const int cc = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = as_f16x8(xb[half_slot(wm * 64 + i * 16 + (lane & 15), cc)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = as_f16x8(wb[half_slot(wn * 64 + i * 16 + (lane & 15), cc)]);
+    };
+    // 16 products of one k-half, one fragment read slotted between every two of them
+    auto mma16 = [&](const f16x8 (&a)[4], const f16x8 (&b)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two matrix products
+        }
+    };
+    load_x(0, 0);
+    load_w(0, 0);
+    load_x(0, 1);
+    load_w(0, 1);
+    load_x(1, 0);
+    load_w(1, 0);
+    load_x(1, 1);
+    load_w(1, 1);
+    load_x(2, 0);
+    load_w(2, 0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // X and W of steps 0, 1 and step 2 half 0 landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    f16x8 a0[4], b0[4], a1[4], b1[4];
+    read_frags(0, 0, a0, b0);
+    // step 0 reloads this stage and half: the reads must be done first
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    auto step = [&](int k) {
+        load_x(k + 3, 0);   // stage k%3 half 0: step k's half 0 was read before B_{k-1}
+        load_w(k + 3, 0);
+        load_x(k + 2, 1);   // stage (k+2)%3 half 1: step k-1's half 1 was read before B_{k-1}
+        load_w(k + 2, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(k, 1, a1, b1);
+        mma16(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(min(k + 1, n_k - 1), 0, a0, b0);
+        mma16(a1, b1);
+    };
+    for (int k = 0; k + 1 < n_k; ++k) {
+        step(k);
+        __builtin_amdgcn_sched_barrier(0);
+        step_barrier();
+    }
+    // The last step's half-0 read of step n_k-1 is dead and may race with its own loads.
+    step(n_k - 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // no LDS load in flight at exit
+
+    // epilogue: lane holds D[4*(l/16)+r][l%16] of block (i, j)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
+        if (col >= out) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = t0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+                if (tok < T) y[(size_t)tok * out + col] = (f16)acc[i][j][r];
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_dense(const void* x, const void* w16, void* y, int64_t out, int64_t in, int64_t batch,
+                             hipStream_t stream) {
+    if (in % 64 != 0) return hipErrorInvalidValue;
+    if (out == 0 || batch == 0) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute((const void*)gemm_dense_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDenseLds);
+    if (e != hipSuccess) return e;
+    const int64_t n_tt = (batch + kDenseBM - 1) / kDenseBM;
+    const int64_t n_tiles = ((out + kDenseBN - 1) / kDenseBN) * n_tt;
+    const int64_t per = (n_tiles + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(gemm_dense_kernel, dim3((unsigned)(per * kXcds)), dim3(kDenseThreads), kDenseLds, stream,
+                       (const f16*)x, (const f16*)w16, (f16*)y, (int)out, (int)in, (int)batch, (int)n_tt,
+                       (int)n_tiles, (int)per);
+    return hipGetLastError();
+}
+
+}  // namespace aqlm

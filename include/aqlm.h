@@ -119,6 +119,30 @@ int aqlm_linear_gemm(const void* codes, const void* codebooks, const void* scale
                      int64_t out, int64_t in, int64_t batch, void* stream);
 
 /*
+ * The same prefill product in two passes, following the page's statement that
+ * the product with the activations runs on the dequantized half-precision
+ * weights ("The AQLM Quantization Algorithm, Explained", MCQ section, Figure
+ * 2): the weights are decoded once into `workspace` (W16[out][in] fp16,
+ * bit-exact as aqlm_linear_decode writes them, the scale applied), then a
+ * dense fp16 matrix-core product y = x W16^T runs with fp32 accumulation and
+ * one rounding to fp16.  Each weight is decoded once instead of once per
+ * 256-token tile.  workspace is caller-owned device memory, 16-byte aligned,
+ * of at least aqlm_gemm_dequant_workspace_bytes bytes; its contents are
+ * overwritten, and calls that share it must not run concurrently.  Every
+ * argument is validated as by aqlm_linear_gemm, and out * (in / g) <
+ * 2^32 (else AQLM_ERR_SHAPE).  A NULL or undersized workspace gives
+ * AQLM_ERR_NULL / AQLM_ERR_SHAPE, a misaligned one AQLM_ERR_ALIGN.  When
+ * in % 64 != 0 the call runs aqlm_linear_gemm instead and does not touch the
+ * workspace.
+ */
+int aqlm_linear_gemm_dequant(const void* codes, const void* codebooks, const void* scales,
+                             const void* x, void* y, void* workspace, int64_t workspace_bytes,
+                             int M, int B, int g, int64_t out, int64_t in, int64_t batch, void* stream);
+
+/* Bytes of workspace aqlm_linear_gemm_dequant needs (out * in * 2; 0 when in % 64 != 0). */
+int aqlm_gemm_dequant_workspace_bytes(int M, int B, int g, int64_t out, int64_t in, int64_t* bytes);
+
+/*
  * Writes the dequantized fp16 weights W16[out][in] to y (bit-exact as stated
  * above).  x must be NULL; batch is ignored.
  */

@@ -343,3 +343,40 @@ def test_lists_fused_workspace_bytes(lib):
         binding.lists_fused_workspace_bytes([], 4096)
     with pytest.raises(ValueError):
         binding.lists_fused_workspace_bytes([64], 4100)
+
+
+def dequant(**kw):
+    a = dict(VALID, ws=A, ws_bytes=16 * 64 * 2)
+    a.update(kw)
+    return int(lib_fn("aqlm_linear_gemm_dequant")(a["codes"], a["codebooks"], a["scales"], a["x"], a["y"], a["ws"],
+                                                  a["ws_bytes"], a["M"], a["B"], a["g"], a["out"], a["n_in"],
+                                                  a["batch"], None))
+
+
+def test_validation_gemm_dequant(lib):
+    for key in ("codes", "codebooks", "scales", "x", "y", "ws"):
+        assert dequant(**{key: 0}) == binding.AQLM_ERR_NULL
+    assert dequant(M=9) == binding.AQLM_ERR_SCHEME
+    assert dequant(ws_bytes=16 * 64 * 2 - 1) == binding.AQLM_ERR_SHAPE
+    assert dequant(n_in=60) == binding.AQLM_ERR_SHAPE
+    assert dequant(batch=-1) == binding.AQLM_ERR_SHAPE
+    assert dequant(out=1 << 24, n_in=4096, ws_bytes=1 << 40) == binding.AQLM_ERR_SHAPE   # out * in / g >= 2^32
+    for key in ("codes", "codebooks", "x", "y", "ws"):
+        assert dequant(**{key: A + 8}) == binding.AQLM_ERR_ALIGN
+    assert dequant(scales=A + 1) == binding.AQLM_ERR_ALIGN
+    # empty problems enqueue nothing and need no workspace
+    assert dequant(out=0, ws=0, ws_bytes=0) == binding.AQLM_OK
+    assert dequant(batch=0, ws=0, ws_bytes=0) == binding.AQLM_OK
+
+
+def test_gemm_dequant_workspace_bytes(lib):
+    assert binding.gemm_dequant_workspace_bytes(2, 8, 8, 4096, 4096) == 4096 * 4096 * 2
+    assert binding.gemm_dequant_workspace_bytes(1, 16, 8, 11008, 4096) == 11008 * 4096 * 2
+    assert binding.gemm_dequant_workspace_bytes(2, 8, 8, 100, 520) == 0      # in % 64 != 0: not used
+    assert binding.gemm_dequant_workspace_bytes(4, 8, 16, 0, 64) == 0
+    n = ctypes.c_int64(0)
+    fn = lib_fn("aqlm_gemm_dequant_workspace_bytes")
+    assert fn(9, 8, 8, 64, 64, ctypes.byref(n)) == binding.AQLM_ERR_SCHEME
+    assert fn(2, 8, 8, -1, 64, ctypes.byref(n)) == binding.AQLM_ERR_SHAPE
+    assert fn(2, 8, 8, 64, 60, ctypes.byref(n)) == binding.AQLM_ERR_SHAPE
+    assert fn(2, 8, 8, 64, 64, None) == binding.AQLM_ERR_NULL
