@@ -22,10 +22,12 @@
 //    which lane l decodes group 8*(q/2) + 2*(l/16) + q%2: the k order inside
 //    each product changes, and the x pieces of one product then lie in one
 //    128-byte line per batch row instead of four;
-//  * the 2x8 codebooks live in LDS, replicated REPL times with entry k of
+//  * the 2x8 codebooks live in LDS, replicated REPL = 8 times with entry k of
 //    replica r at 16-byte slot (2k + m) * REPL + r; lane l reads replica
-//    l % REPL, which spreads the 16 lanes served together over distinct bank
-//    groups; 1x16 codewords are gathered from the L2-resident 1 MiB codebook;
+//    l % REPL, which spreads the lanes served together over distinct bank
+//    groups (8 replicas, 64 KB, measured faster than 16: the smaller copy
+//    into LDS outweighs the extra conflicts); 1x16 codewords are gathered
+//    from the L2-resident 1 MiB codebook;
 //  * per-wave partial tiles are summed in LDS; the row scale is applied once
 //    in fp32 and y is rounded to fp16.
 //
@@ -362,7 +364,7 @@ hipError_t launch_gemv_fused(int scheme, GemvLayers layers, const void* x, int64
     if (layers.n < 1) return hipSuccess;
     deal_workgroups(layers, device_cu_count());
     const int n = (int)in, T = (int)batch;
-    if (scheme == kScheme2x8) return launch_gemv_s<kScheme2x8, 16, RTP>(layers, x, n, T, stream);
+    if (scheme == kScheme2x8) return launch_gemv_s<kScheme2x8, 8, RTP>(layers, x, n, T, stream);
     return launch_gemv_s<kScheme1x16, 1, RTP>(layers, x, n, T, stream);
 }
 
