@@ -11,22 +11,27 @@
 // each weight once.
 //
 // A workgroup owns a 256-token x 128-row output tile and walks k in steps of
-// 64 inputs, each split into two k-halves of 32.  Eight waves each own a
-// 64x64 piece: they copy their share of the X and W halves straight from
-// global memory into LDS (direct-to-LDS loads), read 16-byte fragments and
-// run 16x16x32 fp16 matrix-core products with fp32 accumulators.
+// 64 inputs, each split into two k-halves of 32 for the products.  Eight waves
+// each own a 64x64 piece: they copy their share of the X and W tiles of a step
+// straight from global memory into LDS (direct-to-LDS loads), read 16-byte
+// fragments and run 16x16x32 fp16 matrix-core products with fp32 accumulators.
 //
 // Pipeline (one barrier per step; B_k is the barrier that ends step k):
-//   step k : load X and W of step k+3 half 0 and of step k+2 half 1;
-//            read half 1 of step k, multiply half 0 of step k;
-//            read half 0 of step k+1, multiply half 1 of step k;
+//   step k : load the X and W tiles of step k+2 (whole rows of 128 bytes);
+//            read half 0 of step k while multiplying half 1 of step k-1;
+//            read half 1 of step k while multiplying half 0 of step k;
 //            B_k waits for every load issued before step k.
-// X and W keep three stages each: 96 + 48 = 144 KB of LDS.
+// X and W keep three whole-step stages each: 96 + 48 = 144 KB of LDS.  The
+// products run in the same order as a plain k loop, so the skew changes no
+// result.
 //
-// LDS layout of one k-half of a tile: row r holds 4 chunks of 16 bytes; chunk c
-// sits in slot 4r + (c ^ ((r >> 2) & 3)).  A direct-to-LDS load writes 64
-// consecutive slots (16 whole rows), and the 16 lanes of a fragment read hit
-// 16 distinct bank groups.
+// LDS layout of a stage: row r holds the 8 chunks (16 bytes each) of its 64
+// inputs; chunk c sits in slot 8r + (c ^ ((r >> 1) & 7)).  A direct-to-LDS
+// load writes 64 consecutive slots, 8 whole rows, so each load reads 8 full
+// 128-byte lines (loading the two halves of a row at different times, 16 rows
+// of 64 bytes per load, was measured 15-25 % slower).  The 16 lanes of a
+// fragment read (16 consecutive rows, one chunk) hit 16 distinct 16-byte bank
+// groups.
 //
 // Tile order: consecutive workgroups go to different XCDs, so workgroup b
 // takes tile (b % 8) * per + b / 8 of the token-fastest tile order.  Each XCD
@@ -43,11 +48,11 @@ constexpr int kDenseBM = 256;                // tokens per tile
 constexpr int kDenseBN = 128;                // output rows per tile
 constexpr int kDenseWaves = 8;
 constexpr int kDenseThreads = 64 * kDenseWaves;
-constexpr int kDenseXHalf = kDenseBM * 4;    // 16-byte slots of one X k-half
-constexpr int kDenseWHalf = kDenseBN * 4;    // 16-byte slots of one W k-half
+constexpr int kDenseXStage = kDenseBM * 8;   // 16-byte slots of one X stage (a whole 64-input step)
+constexpr int kDenseWStage = kDenseBN * 8;   // 16-byte slots of one W stage
 constexpr int kDenseStages = 3;
-constexpr int kDenseWOff = kDenseStages * 2 * kDenseXHalf;
-constexpr size_t kDenseLds = (size_t)(kDenseWOff + kDenseStages * 2 * kDenseWHalf) * 16;
+constexpr int kDenseWOff = kDenseStages * kDenseXStage;
+constexpr size_t kDenseLds = (size_t)(kDenseWOff + kDenseStages * kDenseWStage) * 16;
 static_assert(kDenseLds <= 163840, "LDS budget");
 constexpr int kXcds = 8;                     // tile order only; any count gives correct results
 
@@ -56,18 +61,19 @@ constexpr int kXcds = 8;                     // tile order only; any count gives
 constexpr int wait_vm_lgkm0(int n) { return n | (7 << 4); }
 // s_waitcnt lgkmcnt(0) with the vector-memory and export counters at their maxima
 constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
-// loads a wave issues per step: X 2 per half, W 1 per half
+// loads a wave issues per step: 4 of X (32 rows), 2 of W (16 rows)
 constexpr int kDenseLoadsPerStep = 6;
 
-__device__ __forceinline__ int half_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int stage_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
 
 __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
     return (__attribute__((address_space(3))) void*)p;
 }
 
-// B_k: every load issued before this step has landed (this step's own stay in
-// flight), every LDS read of the workgroup is done.
+// B_{k-1}: every load issued before the previous step has landed (the previous
+// step's own stay in flight), every LDS read of the workgroup is done.
 __device__ __forceinline__ void step_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kDenseLoadsPerStep));
     __builtin_amdgcn_s_barrier();
@@ -79,8 +85,8 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
                                                                    int out, int in, int T, int n_tt, int n_tiles,
                                                                    int per_xcd) {
     extern __shared__ u32x4 smem[];
-    u32x4* Xs = smem;                 // [stage 3][half 2][kDenseXHalf]
-    u32x4* Ws = smem + kDenseWOff;    // [stage 3][half 2][kDenseWHalf]
+    u32x4* Xs = smem;                 // [stage 3][kDenseXStage]
+    u32x4* Ws = smem + kDenseWOff;    // [stage 3][kDenseWStage]
     const int tile = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
     if (tile >= n_tiles) return;      // the whole workgroup: the grid is rounded up to kXcds * per_xcd
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -88,27 +94,32 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
     const int t0 = (tile % n_tt) * kDenseBM;
     const int n_k = in / 64;          // the launcher guarantees in % 64 == 0
 
-    // Half h of step j into stage j % 3.  Lane l of a 16-row load writes slot
-    // 64 q + l = 4 rr + (l & 3), which holds chunk c of row rr.
-    const int rr0 = lane >> 2;
-    const int c = (lane & 3) ^ ((lane >> 4) & 3);
-    auto load_x = [&](int j, int h) {
+    // The tiles of step j into stage j % 3.  Load q writes slots 64 q .. 64 q + 63:
+    // lane l fills slot 64 q + l, which holds chunk (l % 8) ^ ((r >> 1) & 7) of row
+    // r = 8 q + l / 8, so the 8 lanes of a row read its whole 128-byte line.
+    const int rsub = lane >> 3;
+    auto load_step = [&](int j) {
         const int jc = min(j, n_k - 1);
-        u32x4* dst = Xs + ((j % kDenseStages) * 2 + h) * kDenseXHalf;
+        u32x4* dx = Xs + (j % kDenseStages) * kDenseXStage;
+        u32x4* dw = Ws + (j % kDenseStages) * kDenseWStage;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = 4 * wave + i;
+            const int r = 8 * q + rsub;
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            const int tok = min(t0 + r, T - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)tok * in + (size_t)(8 * jc + c) * kGroup),
+                                             lds_ptr(dx + 64 * q), 16, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int q = 2 * wave + i;
-            const int tok = min(t0 + 16 * q + rr0, T - 1);
-            __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)tok * in + (size_t)(8 * jc + 4 * h + c) * kGroup),
-                                             lds_ptr(dst + 64 * q), 16, 0, 0);
+            const int r = 8 * q + rsub;
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            const int row = min(n0 + r, out - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(w + (size_t)row * in + (size_t)(8 * jc + c) * kGroup),
+                                             lds_ptr(dw + 64 * q), 16, 0, 0);
         }
-    };
-    auto load_w = [&](int j, int h) {
-        const int jc = min(j, n_k - 1);
-        u32x4* dst = Ws + ((j % kDenseStages) * 2 + h) * kDenseWHalf;
-        const int row = min(n0 + 16 * wave + rr0, out - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(w + (size_t)row * in + (size_t)(8 * jc + 4 * h + c) * kGroup),
-                                         lds_ptr(dst + 64 * wave), 16, 0, 0);
     };
 
     const int wm = wave >> 1, wn = wave & 1;
@@ -119,13 +130,13 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // fragments of half h of step j: lane l holds A[l%16][8(l/16)..] and B[8(l/16)..][l%16]
     auto read_frags = [&](int j, int h, f16x8 (&a)[4], f16x8 (&b)[4]) {
-        const u32x4* xb = Xs + ((j % kDenseStages) * 2 + h) * kDenseXHalf;
-        const u32x4* wb = Ws + ((j % kDenseStages) * 2 + h) * kDenseWHalf;
-        const int cc = lane >> 4;
+        const u32x4* xb = Xs + (j % kDenseStages) * kDenseXStage;
+        const u32x4* wb = Ws + (j % kDenseStages) * kDenseWStage;
+        const int cc = 4 * h + (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = as_f16x8(xb[half_slot(wm * 64 + i * 16 + (lane & 15), cc)]);
+        for (int i = 0; i < 4; ++i) a[i] = as_f16x8(xb[stage_slot(wm * 64 + i * 16 + (lane & 15), cc)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = as_f16x8(wb[half_slot(wn * 64 + i * 16 + (lane & 15), cc)]);
+        for (int i = 0; i < 4; ++i) b[i] = as_f16x8(wb[stage_slot(wn * 64 + i * 16 + (lane & 15), cc)]);
     };
     // 16 products of one k-half, one fragment read slotted between every two of them
     auto mma16 = [&](const f16x8 (&a)[4], const f16x8 (&b)[4]) {
@@ -139,43 +150,31 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two matrix products
         }
     };
-    load_x(0, 0);
-    load_w(0, 0);
-    load_x(0, 1);
-    load_w(0, 1);
-    load_x(1, 0);
-    load_w(1, 0);
-    load_x(1, 1);
-    load_w(1, 1);
-    load_x(2, 0);
-    load_w(2, 0);
+    load_step(0);
+    load_step(1);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // X and W of steps 0, 1 and step 2 half 0 landed
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // steps 0 and 1 landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     f16x8 a0[4], b0[4], a1[4], b1[4];
+    // step 0: both halves of stage 0 read, half 0 multiplied
+    load_step(2);
+    __builtin_amdgcn_sched_barrier(0);
     read_frags(0, 0, a0, b0);
-    // step 0 reloads this stage and half: the reads must be done first
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    auto step = [&](int k) {
-        load_x(k + 3, 0);   // stage k%3 half 0: step k's half 0 was read before B_{k-1}
-        load_w(k + 3, 0);
-        load_x(k + 2, 1);   // stage (k+2)%3 half 1: step k-1's half 1 was read before B_{k-1}
-        load_w(k + 2, 1);
+    read_frags(0, 1, a1, b1);
+    mma16(a0, b0);
+    for (int k = 1; k < n_k; ++k) {
+        step_barrier();
+        load_step(k + 2);       // stage (k-1) % 3: step k-1 was read before B_{k-1}
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(k, 0, a0, b0);
+        mma16(a1, b1);          // half 1 of step k-1
         __builtin_amdgcn_sched_barrier(0);
         read_frags(k, 1, a1, b1);
-        mma16(a0, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(min(k + 1, n_k - 1), 0, a0, b0);
-        mma16(a1, b1);
-    };
-    for (int k = 0; k + 1 < n_k; ++k) {
-        step(k);
-        __builtin_amdgcn_sched_barrier(0);
-        step_barrier();
+        mma16(a0, b0);          // half 0 of step k
     }
-    // The last step's half-0 read of step n_k-1 is dead and may race with its own loads.
-    step(n_k - 1);
+    mma16(a1, b1);              // half 1 of the last step
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // no LDS load in flight at exit
 
