@@ -24,21 +24,24 @@
 // different waves.
 //
 // Pipeline (one barrier per step; B_k is the barrier that ends step k):
-//   consumer step k : load X(k+3) half 0 and X(k+2) half 1;
+//   consumer step k : load the X tile of step k+2 (whole 128-byte rows);
+//                     read half 0 of step k, multiply half 1 of step k-1;
 //                     read half 1 of step k, multiply half 0 of step k;
-//                     read half 0 of step k+1, multiply half 1 of step k;
 //                     B_k waits for every X load issued before step k.
 //   producer step k : load the codes of step k+kRing;
-//                     decode W(k+2) half 0 and W(k+1) half 1;
-//                     B_k waits for the codes of step k+3.
-// Every X half thus has two steps to arrive, every code load about kRing-3.
-// X keeps three stages, W two (a W half is written one step before it is
-// read), the code ring kRing steps: 96 + 32 + 24 + 8 (codebooks) = 160 KB.
+//                     decode the whole W tile of step k+1;
+//                     B_k waits for the codes of step k+2.
+// X tiles thus have two steps to arrive, code loads about kRing-2.  X keeps
+// three stages, W two (a W tile is written one step before it is read), the
+// code ring kRing steps: 96 + 32 + 24 + 8 (codebooks) = 160 KB.  The products
+// run in the order of a plain k loop.
 //
-// LDS layout of one k-half of a tile: row r holds 4 chunks of 16 bytes; chunk c
-// sits in slot 4r + (c ^ ((r >> 2) & 3)).  A direct-to-LDS load writes 64
-// consecutive slots (16 whole rows), and the 16 lanes of a fragment read hit
-// 16 distinct bank groups.
+// LDS layout of a stage: row r holds the 8 chunks (16 bytes each) of its 64
+// inputs; chunk c sits in slot 8r + (c ^ ((r >> 1) & 7)).  A direct-to-LDS
+// load writes 64 consecutive slots, 8 whole rows, so each X load reads 8 full
+// 128-byte lines (loading the two halves of a row at different times, 16 rows
+// of 64 bytes per load, was measured 16-21 % slower).  The 16 lanes of a
+// fragment read (16 consecutive rows, one chunk) hit 16 distinct bank groups.
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
@@ -51,14 +54,14 @@ constexpr int kPipeBN = 128;                 // output rows per tile
 constexpr int kPipeConsumers = 8;            // consumer waves
 constexpr int kPipeProducers = 4;            // producer waves
 constexpr int kPipeThreads = 64 * (kPipeConsumers + kPipeProducers);
-constexpr int kPipeXHalf = kPipeBM * 4;      // 16-byte slots of one X k-half
-constexpr int kPipeWHalf = kPipeBN * 4;      // 16-byte slots of one W k-half
+constexpr int kPipeXStage = kPipeBM * 8;     // 16-byte slots of one X stage (a whole step)
+constexpr int kPipeWStage = kPipeBN * 8;     // 16-byte slots of one W stage
 constexpr int kPipeWStages = 2;
 constexpr int kPipeRing = 12;                // steps of codes held in LDS
 constexpr int kPipeCb = 2 * kCodewords2x8;   // codebook slots: codeword k of codebook m at 2k+m
 constexpr int kPipeXOff = 0;
-constexpr int kPipeWOff = kPipeXOff + 3 * 2 * kPipeXHalf;
-constexpr int kPipeRingOff = kPipeWOff + kPipeWStages * 2 * kPipeWHalf;
+constexpr int kPipeWOff = kPipeXOff + 3 * kPipeXStage;
+constexpr int kPipeRingOff = kPipeWOff + kPipeWStages * kPipeWStage;
 constexpr int kPipeCbOff = kPipeRingOff + kPipeRing * kPipeBN;
 constexpr size_t kPipeLds = (size_t)(kPipeCbOff + kPipeCb) * 16;
 static_assert(kPipeLds <= 163840, "LDS budget");
@@ -66,7 +69,7 @@ static_assert(kPipeLds <= 163840, "LDS budget");
 // s_waitcnt lgkmcnt(0) with the vector-memory and export counters left at their maxima
 constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
 
-__device__ __forceinline__ int half_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int stage_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
 
 __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
     return (__attribute__((address_space(3))) void*)p;
@@ -77,8 +80,8 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
     const f16* __restrict__ scales, const f16* __restrict__ x, f16* __restrict__ y,
     int out, int in, int T) {
     extern __shared__ u32x4 smem[];
-    u32x4* Xs = smem + kPipeXOff;       // [stage 3][half 2][kPipeXHalf]
-    u32x4* Ws = smem + kPipeWOff;       // [stage 2][half 2][kPipeWHalf]
+    u32x4* Xs = smem + kPipeXOff;       // [stage 3][kPipeXStage]
+    u32x4* Ws = smem + kPipeWOff;       // [stage 2][kPipeWStage]
     u32x4* ring = smem + kPipeRingOff;  // [kPipeRing][row 128] : the 8 group codes of a row, 16 bytes
     u32x4* cb = smem + kPipeCbOff;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -107,13 +110,13 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
                                                  lds_ptr(slot + (2 * pw + i) * 64), 4, 0, 0);
             }
         };
-        // thread p decodes chunks c0, c0+1 of row r in one half of each of two steps;
-        // every LDS read is issued before the first write so the lookups overlap
+        // thread p decodes chunks c0 .. c0+3 of row r of step j; every LDS read is
+        // issued before the first write so the lookups overlap
         const int p = tid - 64 * kPipeConsumers;
-        const int r = p >> 1, c0 = 2 * (p & 1);
-        auto decode2 = [&](int ja, int ha, int jb, int hb) {
-            const uint32_t ca = reinterpret_cast<const uint32_t*>(ring + (ja % kPipeRing) * kPipeBN + r)[(4 * ha + c0) >> 1];
-            const uint32_t cw = reinterpret_cast<const uint32_t*>(ring + (jb % kPipeRing) * kPipeBN + r)[(4 * hb + c0) >> 1];
+        const int r = p >> 1, c0 = 4 * (p & 1);
+        auto decode_step = [&](int j) {
+            const uint32_t* cr = reinterpret_cast<const uint32_t*>(ring + (j % kPipeRing) * kPipeBN + r);
+            const uint32_t ca = cr[c0 >> 1], cw = cr[(c0 >> 1) + 1];
             f16x8 e[8];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -122,31 +125,26 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
                 e[4 + 2 * q] = as_f16x8(cb[2 * ((cw >> (16 * q)) & 0xff)]);
                 e[5 + 2 * q] = as_f16x8(cb[2 * ((cw >> (16 * q + 8)) & 0xff) + 1]);
             }
-            u32x4* da = Ws + ((ja % kPipeWStages) * 2 + ha) * kPipeWHalf;
-            u32x4* db = Ws + ((jb % kPipeWStages) * 2 + hb) * kPipeWHalf;
+            u32x4* d = Ws + (j % kPipeWStages) * kPipeWStage;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                da[half_slot(r, c0 + q)] = as_u32x4(e[2 * q] + e[2 * q + 1]);
-                db[half_slot(r, c0 + q)] = as_u32x4(e[4 + 2 * q] + e[5 + 2 * q]);
-            }
+            for (int q = 0; q < 4; ++q) d[stage_slot(r, c0 + q)] = as_u32x4(e[2 * q] + e[2 * q + 1]);
         };
 #pragma unroll
         for (int j = 0; j < kPipeRing; ++j) load_codes(j);
-        // P1: codebook copy staged, codes of steps 0 and 1 landed
+        // P1: codebook copy staged, codes of step 0 landed
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kPipeRing - 1)) : "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        decode_step(0);
+        // P2: W(0) written, codes of step 1 landed
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kPipeRing - 2)) : "memory");
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        decode2(0, 0, 0, 1);
-        decode2(1, 0, 1, 0);
-        // P2: W(0), W(1) half 0 written, codes of step 2 landed
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kPipeRing - 3)) : "memory");
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         for (int k = 0; k + 1 < n_k; ++k) {
-            load_codes(k + kPipeRing);          // replaces step k's codes, last read before B_{k-1}
+            load_codes(k + kPipeRing);          // replaces step k's codes, decoded before B_{k-1}
             __builtin_amdgcn_sched_barrier(0);
-            decode2(k + 2, 0, k + 1, 1);
+            decode_step(k + 1);                 // stage (k+1) % 2: step k-1's W was read before B_{k-1}
             __builtin_amdgcn_sched_barrier(0);
-            // B_k: W written, codes of step k+3 landed (issued kPipeRing-3 steps ago or earlier)
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kPipeRing - 3)) : "memory");
+            // B_k: W(k+1) written, codes of step k+2 landed (issued kPipeRing-2 steps ago or earlier)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kPipeRing - 2)) : "memory");
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load in flight at exit
@@ -155,17 +153,18 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
 
     // ------------------------------ consumers ------------------------------
     const int wm = wave >> 1, wn = wave & 1;
-    // X half h of step j into stage j % 3: this wave writes rows 32*wave .. 32*wave+31
-    auto load_x = [&](int j, int h) {
+    // X of step j into stage j % 3: load q writes slots 64q .. 64q+63, lane l the chunk
+    // (l % 8) ^ ((rr >> 1) & 7) of row rr = 8q + l/8 (8 whole 128-byte lines per load)
+    auto load_x = [&](int j) {
         const int jc = min(j, n_k - 1);
-        u32x4* dst = Xs + ((j % 3) * 2 + h) * kPipeXHalf;
+        u32x4* dst = Xs + (j % 3) * kPipeXStage;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = 2 * wave + i;                     // 16 rows per direct load
-            const int rr = 16 * q + (lane >> 2);
-            const int c = (lane & 3) ^ ((lane >> 4) & 3);   // slot 4*rr + (lane & 3) holds chunk c
+        for (int i = 0; i < 4; ++i) {
+            const int q = 4 * wave + i;
+            const int rr = 8 * q + (lane >> 3);
+            const int c = (lane & 7) ^ ((rr >> 1) & 7);
             const int tok = min(t0 + rr, T - 1);
-            __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)tok * in + (size_t)(8 * jc + 4 * h + c) * kGroup),
+            __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)tok * in + (size_t)(8 * jc + c) * kGroup),
                                              lds_ptr(dst + 64 * q), 16, 0, 0);
         }
     };
@@ -174,17 +173,15 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // fragments of half h of step j: lane l holds A[l%16][8(l/16)..] and B[8(l/16)..][l%16]
     auto read_frags = [&](int j, int h, f16x8 (&a)[4], f16x8 (&b)[4]) {
-        const u32x4* xb = Xs + ((j % 3) * 2 + h) * kPipeXHalf;
-        const u32x4* wb = Ws + ((j % kPipeWStages) * 2 + h) * kPipeWHalf;
-        const int c = lane >> 4;
+        const u32x4* xb = Xs + (j % 3) * kPipeXStage;
+        const u32x4* wb = Ws + (j % kPipeWStages) * kPipeWStage;
+        const int c = 4 * h + (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = as_f16x8(xb[half_slot(wm * 64 + i * 16 + (lane & 15), c)]);
+        for (int i = 0; i < 4; ++i) a[i] = as_f16x8(xb[stage_slot(wm * 64 + i * 16 + (lane & 15), c)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = as_f16x8(wb[half_slot(wn * 64 + i * 16 + (lane & 15), c)]);
+        for (int i = 0; i < 4; ++i) b[i] = as_f16x8(wb[stage_slot(wn * 64 + i * 16 + (lane & 15), c)]);
     };
-    // 16 products of one k-half, one fragment read slotted between every two of them
     auto mma16 = [&](const f16x8 (&a)[4], const f16x8 (&b)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -196,35 +193,31 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two matrix products
         }
     };
-    load_x(0, 0);
-    load_x(0, 1);
-    load_x(1, 0);
-    load_x(1, 1);
-    load_x(2, 0);
+    load_x(0);
+    load_x(1);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // P1: codebook copy staged
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");     // P2: X(0), X(1), X(2) half 0 landed
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");     // P2: X(0), X(1) landed, W(0) written
     f16x8 a0[4], b0[4], a1[4], b1[4];
+    load_x(2);
+    __builtin_amdgcn_sched_barrier(0);
     read_frags(0, 0, a0, b0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    auto step = [&](int k) {
-        load_x(k + 3, 0);   // stage k%3 half 0: step k's half 0 was read before B_{k-1}
-        load_x(k + 2, 1);   // stage (k+2)%3 half 1: step k-1's half 1 was read before B_{k-1}
+    read_frags(0, 1, a1, b1);
+    mma16(a0, b0);
+    for (int k = 1; k < n_k; ++k) {
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(k, 1, a1, b1);
-        mma16(a0, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(min(k + 1, n_k - 1), 0, a0, b0);
-        mma16(a1, b1);
-    };
-    for (int k = 0; k + 1 < n_k; ++k) {
-        step(k);
-        __builtin_amdgcn_sched_barrier(0);
-        // B_k: the four X loads of this step stay in flight, all earlier ones have landed
+        // B_{k-1}: the four X loads of step k-1 stay in flight, all earlier ones have landed
         asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        load_x(k + 2);          // stage (k-1) % 3: step k-1 was read before B_{k-1}
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(k, 0, a0, b0);
+        mma16(a1, b1);          // half 1 of step k-1
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(k, 1, a1, b1);
+        mma16(a0, b0);          // half 0 of step k
     }
-    // The last step's half-0 read of step n_k-1 is dead and may race with its own X loads.
-    step(n_k - 1);
+    mma16(a1, b1);              // half 1 of the last step
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load in flight at exit
 
     // epilogue: lane holds D[4*(l/16)+r][l%16] of block (i, j)
