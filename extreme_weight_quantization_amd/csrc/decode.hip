@@ -9,7 +9,8 @@
 //
 // One thread produces one group (8 fp16 = one 16-byte store).  The 2x8
 // codebooks (8 KB) are staged in LDS; 1x16 codewords are gathered from the
-// 1 MiB codebook through L2.  The kernel is bound by the W16 write stream.
+// 1 MiB codebook through L2.  The kernel is bound by the W16 write stream, which
+// is written with non-temporal stores.
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
@@ -49,7 +50,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint8_t* __restrict__
         f16x8 o;
 #pragma unroll
         for (int t = 0; t < kGroup; ++t) o[t] = (f16)__fmul_rn(v[t], s);
-        *reinterpret_cast<u32x4*>(w + (size_t)gid * kGroup) = as_u32x4(o);
+        // non-temporal: the W16 stream must not evict the codebook from L2 (1x16 gathers
+        // it from there) or the codes; measured 3-19 % faster on the 7B shapes
+        __builtin_nontemporal_store(as_u32x4(o), reinterpret_cast<u32x4*>(w + (size_t)gid * kGroup));
     }
 }
 

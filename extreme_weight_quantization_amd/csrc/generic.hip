@@ -125,7 +125,13 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(const uint8_t* __re
                 f16x8 o;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) o[t] = (f16)__fmul_rn(v[p * 8 + t], s);
-                *reinterpret_cast<f16x8*>(dst + p * 8) = o;
+                // g <= 16: non-temporal, so the W16 stream does not evict the codebooks from L2;
+                // g = 32: plain stores, which L2 merges into whole lines (a lane's four
+                // 16-byte pieces are 64 bytes apart within one store instruction)
+                if constexpr (G <= 16)
+                    __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(dst + p * 8));
+                else
+                    *reinterpret_cast<f16x8*>(dst + p * 8) = o;
             }
         } else {
 #pragma unroll
