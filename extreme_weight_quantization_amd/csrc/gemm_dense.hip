@@ -139,6 +139,7 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
         for (int i = 0; i < 4; ++i) b[i] = as_f16x8(wb[stage_slot(wn * 64 + i * 16 + (lane & 15), cc)]);
     };
     // 16 products of one k-half, one fragment read slotted between every two of them
+    // (product, read, product: 1-7 % faster than read, product, product)
     auto mma16 = [&](const f16x8 (&a)[4], const f16x8 (&b)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -146,8 +147,9 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix product
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two matrix products
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix product
         }
     };
     load_step(0);

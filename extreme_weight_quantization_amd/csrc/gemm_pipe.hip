@@ -188,9 +188,10 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < 8; ++q) {   // product, read, product: 3-7 % faster than read, product, product
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix product
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two matrix products
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix product
         }
     };
     load_x(0);
