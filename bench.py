@@ -342,8 +342,8 @@ def main():
                     help="also run a plain 64 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; layers would shard by "
+              "output rows with nothing exchanged (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
