@@ -33,6 +33,9 @@
 // fragment read (16 consecutive rows, one chunk) hit 16 distinct 16-byte bank
 // groups.
 //
+// Epilogue (out % 8 == 0): after a last barrier each wave passes its 64x64 tile
+// through LDS and stores whole 128-byte rows of y, 16 bytes per lane.
+//
 // Tile order: consecutive workgroups go to different XCDs, so workgroup b
 // takes tile (b % 8) * per + b / 8 of the token-fastest tile order.  Each XCD
 // then holds a contiguous run of row tiles with all their token tiles: its L2
@@ -177,10 +180,43 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
         mma16(a0, b0);          // half 0 of step k
     }
     mma16(a1, b1);              // half 1 of the last step
+
+    if (out % 8 == 0) {
+        // Every load of every wave has landed and every fragment read is done, so the
+        // stages are free: each wave's 64x64 tile goes through LDS (fp16, rows of 64 + 8
+        // padding) and leaves as 16-byte stores, 8 lanes per 128-byte row of y.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        constexpr int kEpiStride = 72;
+        f16* etile = reinterpret_cast<f16*>(smem) + wave * 64 * kEpiStride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    etile[(i * 16 + 4 * (lane >> 4) + r) * kEpiStride + j * 16 + (lane & 15)] = (f16)acc[i][j][r];
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        const int c8 = (lane & 7) * 8;
+        const int col = n0 + wn * 64 + c8;
+        if (col < out) {   // out % 8 == 0: a chunk is wholly inside or wholly outside
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int rr = it * 8 + (lane >> 3);
+                const int tok = t0 + wm * 64 + rr;
+                if (tok < T)
+                    *reinterpret_cast<u32x4*>(y + (size_t)tok * out + col) =
+                        *reinterpret_cast<const u32x4*>(etile + rr * kEpiStride + c8);
+            }
+        }
+        return;
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // no LDS load in flight at exit
 
-    // epilogue: lane holds D[4*(l/16)+r][l%16] of block (i, j)
+    // rows not a multiple of 8: lane holds D[4*(l/16)+r][l%16] of block (i, j), stored directly
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int col = n0 + wn * 64 + j * 16 + (lane & 15);
