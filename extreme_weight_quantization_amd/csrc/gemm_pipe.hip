@@ -36,6 +36,11 @@
 // code ring kRing steps: 96 + 32 + 24 + 8 (codebooks) = 160 KB.  The products
 // run in the order of a plain k loop.
 //
+// Epilogue (out % 8 == 0): producers and consumers meet at a last barrier; then
+// each consumer wave passes its scaled 64x64 tile through LDS and stores whole
+// 128-byte rows of y, 16 bytes per lane (2-byte stores per lane wrote 1.47x the
+// bytes of y on 11008 rows: partial lines).
+//
 // LDS layout of a stage: row r holds the 8 chunks (16 bytes each) of its 64
 // inputs; chunk c sits in slot 8r + (c ^ ((r >> 1) & 7)).  A direct-to-LDS
 // load writes 64 consecutive slots, 8 whole rows, so each X load reads 8 full
@@ -147,7 +152,11 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
             asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * (kPipeRing - 2)) : "memory");
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load in flight at exit
+        if (out % 8 == 0) {   // the consumers' epilogue barrier: LDS is free after it
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load in flight at exit
+        }
         return;
     }
 
@@ -219,9 +228,42 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
         mma16(a0, b0);          // half 0 of step k
     }
     mma16(a1, b1);              // half 1 of the last step
+    if (out % 8 == 0) {
+        // all loads landed, all fragment reads and W writes done (producers join this
+        // barrier): each wave's scaled 64x64 tile goes through LDS and leaves as 16-byte
+        // stores, 8 lanes per 128-byte row of y
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        constexpr int kEpiStride = 72;
+        f16* etile = reinterpret_cast<f16*>(smem) + wave * 64 * kEpiStride;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int colj = min(n0 + wn * 64 + j * 16 + (lane & 15), out - 1);
+            const float s = (float)scales[colj];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    etile[(i * 16 + 4 * (lane >> 4) + rr) * kEpiStride + j * 16 + (lane & 15)] = (f16)(acc[i][j][rr] * s);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        const int c8 = (lane & 7) * 8;
+        const int col = n0 + wn * 64 + c8;
+        if (col < out) {
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int r8 = it * 8 + (lane >> 3);
+                const int tok = t0 + wm * 64 + r8;
+                if (tok < T)
+                    *reinterpret_cast<u32x4*>(y + (size_t)tok * out + col) =
+                        *reinterpret_cast<const u32x4*>(etile + r8 * kEpiStride + c8);
+            }
+        }
+        return;
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load in flight at exit
 
-    // epilogue: lane holds D[4*(l/16)+r][l%16] of block (i, j)
+    // rows not a multiple of 8: lane holds D[4*(l/16)+r][l%16] of block (i, j), stored directly
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int col = n0 + wn * 64 + j * 16 + (lane & 15);
