@@ -105,19 +105,28 @@ __device__ __forceinline__ void stage_codebook(f16* dst, const f16* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Decode: one thread per group, bit-exact.
-template <int G, int CB>
-__global__ __launch_bounds__(256) void decode_generic_kernel(const uint8_t* __restrict__ codes,
-                                                             const f16* __restrict__ codebooks,
-                                                             const f16* __restrict__ scales,
-                                                             f16* __restrict__ w, uint32_t n_groups,
-                                                             uint32_t n_grp_row, int M, int B) {
+// Decode: one thread per group, bit-exact.  LDS: codebooks of at most
+// kGemvLdsCodebook bytes are copied to LDS first (1024-thread workgroups), so the
+// lookups are LDS reads instead of L2 gathers.
+template <int G, int CB, bool LDS>
+__global__ __launch_bounds__(1024) void decode_generic_kernel(const uint8_t* __restrict__ codes,
+                                                              const f16* __restrict__ codebooks,
+                                                              const f16* __restrict__ scales,
+                                                              f16* __restrict__ w, uint32_t n_groups,
+                                                              uint32_t n_grp_row, int M, int B) {
+    extern __shared__ u32x4 smem[];
+    const f16* cb = codebooks;
+    if constexpr (LDS) {
+        f16* cbl = reinterpret_cast<f16*>(smem);
+        stage_codebook(cbl, codebooks, (size_t)M << B << __builtin_ctz(G));
+        cb = cbl;
+    }
     const uint32_t mask = (1u << B) - 1u;
     const uint32_t stride = gridDim.x * blockDim.x;
     for (uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x; gid < n_groups; gid += stride) {
         const float s = (float)scales[gid / n_grp_row];
         float v[G];
-        group_weights<G, CB>(codes, (size_t)gid * M, codebooks, M, B, mask, v);
+        group_weights<G, CB>(codes, (size_t)gid * M, cb, M, B, mask, v);
         f16* dst = w + (size_t)gid * G;
         if constexpr (G >= 8) {
 #pragma unroll
@@ -348,10 +357,26 @@ hipError_t decode_g(const GenericScheme& sc, const void* codes, const void* code
                     void* w, int64_t out, int64_t in, hipStream_t stream) {
     const uint32_t n_grp_row = (uint32_t)(in / G);
     const uint64_t n_groups = (uint64_t)out * n_grp_row;
+    const size_t lds = codebook_bytes(sc);
+    if (lds <= kGemvLdsCodebook) {   // codebooks in LDS: one or two 1024-thread workgroups per CU
+        auto kern = decode_generic_kernel<G, CB, true>;
+        if (lds > 65536) {
+            const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        uint64_t blocks = (n_groups + 1023) / 1024;
+        const uint64_t max_blocks = (uint64_t)device_cu_count() * (lds <= 65536 ? 2 : 1);
+        if (blocks > max_blocks) blocks = max_blocks;
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(1024), lds, stream, (const uint8_t*)codes,
+                           (const f16*)codebooks, (const f16*)scales, (f16*)w, (uint32_t)n_groups, n_grp_row, sc.M,
+                           sc.B);
+        return hipGetLastError();
+    }
     uint64_t blocks = (n_groups + 255) / 256;
     const uint64_t max_blocks = (uint64_t)device_cu_count() * 16;
     if (blocks > max_blocks) blocks = max_blocks;
-    hipLaunchKernelGGL((decode_generic_kernel<G, CB>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((decode_generic_kernel<G, CB, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales, (f16*)w,
                        (uint32_t)n_groups, n_grp_row, sc.M, sc.B);
     return hipGetLastError();
