@@ -40,4 +40,18 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// A generic pointer into the workgroup's LDS as the LDS address space, for the
+// direct-to-LDS loads (__builtin_amdgcn_global_load_lds).
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
+    return (__attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt immediates for __builtin_amdgcn_s_waitcnt, which, unlike a wait in
+// inline assembly, the compiler's own wait placement sees.  vmcnt sits in bits
+// 0-3 and 14-15, expcnt in 4-6, lgkmcnt in 8-11.
+// vmcnt(n) lgkmcnt(0), the export counter at its maximum (n < 16):
+constexpr int wait_vm_lgkm0(int n) { return n | (7 << 4); }
+// lgkmcnt(0), the vector-memory and export counters at their maxima:
+constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
+
 }  // namespace aqlm

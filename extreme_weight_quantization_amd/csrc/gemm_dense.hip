@@ -59,19 +59,10 @@ constexpr size_t kDenseLds = (size_t)(kDenseWOff + kDenseStages * kDenseWStage) 
 static_assert(kDenseLds <= 163840, "LDS budget");
 constexpr int kXcds = 8;                     // tile order only; any count gives correct results
 
-// s_waitcnt vmcnt(n) lgkmcnt(0), export counter at its maximum (n < 16).  The
-// builtin, unlike inline assembly, is seen by the compiler's own wait placement.
-constexpr int wait_vm_lgkm0(int n) { return n | (7 << 4); }
-// s_waitcnt lgkmcnt(0) with the vector-memory and export counters at their maxima
-constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
 // loads a wave issues per step: 4 of X (32 rows), 2 of W (16 rows)
 constexpr int kDenseLoadsPerStep = 6;
 
 __device__ __forceinline__ int stage_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
-
-__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
-    return (__attribute__((address_space(3))) void*)p;
-}
 
 // B_{k-1}: every load issued before the previous step has landed (the previous
 // step's own stay in flight), every LDS read of the workgroup is done.

@@ -71,14 +71,7 @@ constexpr int kPipeCbOff = kPipeRingOff + kPipeRing * kPipeBN;
 constexpr size_t kPipeLds = (size_t)(kPipeCbOff + kPipeCb) * 16;
 static_assert(kPipeLds <= 163840, "LDS budget");
 
-// s_waitcnt lgkmcnt(0) with the vector-memory and export counters left at their maxima
-constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (7 << 4);
-
 __device__ __forceinline__ int stage_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
-
-__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
-    return (__attribute__((address_space(3))) void*)p;
-}
 
 __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
     const uint8_t* __restrict__ codes, const f16* __restrict__ codebooks,

@@ -16,18 +16,22 @@
 //    activation operand (x, batch padded to 16 columns) in registers while
 //    they run through the workgroup's row tiles;
 //  * one 16-byte load gives lane l the codes of groups 8*(l/16) .. 8*(l/16)+7
-//    of its slab in row l%16.  Below batch 8, lane l decodes group
-//    8*(l/16) + q for the q-th product.  From batch 8 up, the four lanes of a
-//    row first transpose their 4-byte words (two cross-row lane swaps), after
-//    which lane l decodes group 8*(q/2) + 2*(l/16) + q%2: the k order inside
-//    each product changes, and the x pieces of one product then lie in one
-//    128-byte line per batch row instead of four;
-//  * the 2x8 codebooks live in LDS, replicated REPL = 8 times with entry k of
+//    of its slab in row l%16; lane l decodes group 8*(l/16) + q for the q-th
+//    product;
+//  * the x operand gives lane l batch row l%16, so the 16 lanes of a quarter
+//    read 16 different rows.  At batch 1-2 (2x8) few lanes are active and x
+//    is loaded straight into registers; otherwise each wave first copies its
+//    slab's x rows into an LDS stage of its own with direct-to-LDS loads in
+//    which four consecutive lanes read 64 contiguous bytes of one row, then
+//    reads the operand layout from the stage (a direct load at batch 16
+//    looks up one cache line per lane, which made x the largest cost);
+//  * the 2x8 codebooks live in LDS, replicated REPL times with entry k of
 //    replica r at 16-byte slot (2k + m) * REPL + r; lane l reads replica
 //    l % REPL, which spreads the lanes served together over distinct bank
-//    groups (8 replicas, 64 KB, measured faster than 16: the smaller copy
-//    into LDS outweighs the extra conflicts); 1x16 codewords are gathered
-//    from the L2-resident 1 MiB codebook;
+//    groups.  REPL = 8 (64 KB, measured faster than 16: the smaller copy into
+//    LDS outweighs the extra conflicts) up to batch 8; with the 16-row x
+//    stage (128 KB) above batch 8 only 4 replicas fit.  1x16 codewords are
+//    gathered from the L2-resident 1 MiB codebook;
 //  * per-wave partial tiles are summed in LDS; the row scale is applied once
 //    in fp32 and y is rounded to fp16.
 //
@@ -38,6 +42,8 @@
 // would, so the results are bit-identical to separate launches.  The launch
 // and the first-load, codebook-staging and reduction latencies are then paid
 // once per group of layers instead of once per layer.
+#include <algorithm>
+
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
@@ -48,6 +54,19 @@ constexpr int kGemvThreads = kGemvWaves * kWave;
 constexpr int kSlabGroups = 32;          // groups per slab (8 products x 4 k-quarters)
 constexpr int kRowTile = 16;
 constexpr int kRedFloats = kRowTile * 16; // one 16x16 fp32 tile per wave
+
+// How a wave gets the activation operand of a slab (x of 16 batch columns x 32
+// groups) into registers:
+//   kXDirect      16-byte loads straight into the operand layout;
+//   kXStaged8/16  direct-to-LDS loads of the slab's first 8 or 16 batch rows into
+//                 a stage of this wave (each 4 consecutive lanes read 64
+//                 contiguous bytes of one row), then LDS reads into the operand
+//                 layout.
+// The operand layout puts a different batch row in each of 16 consecutive
+// lanes, so a direct load looks up one cache line per active lane; the staged
+// load looks up one per four lanes.
+enum XMode : int { kXDirect = 0, kXStaged8 = 1, kXStaged16 = 2 };
+constexpr int kXStageSlots(int xm) { return xm == kXStaged16 ? 16 * kSlabGroups : xm == kXStaged8 ? 8 * kSlabGroups : 0; }
 
 // Loads the 8 two-byte codes of a lane's chunk (row, groups g0 .. g0+7),
 // packed two per 32-bit word.  The load is unconditional, with the row and
@@ -70,23 +89,8 @@ __device__ __forceinline__ u32x4 load_codes(const uint8_t* __restrict__ codes, i
     }
 }
 
-// The four 16-lane rows of a wave hold words 4k .. 4k+3 (row k) of a 16-word
-// slab row; afterwards row k holds words k, k+4, k+8, k+12.  Each swap
-// exchanges one register between two rows at the same lane position: first
-// rows {0,1} with {2,3}, then rows {0,2} with {1,3}.
-__device__ __forceinline__ u32x4 transpose_rows4(const u32x4 v) {
-    const auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
-    const auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
-    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-    return u32x4{c[0], c[1], d[0], d[1]};
-}
-
 // Group of product q (0..7) in the slab for the lane of k-quarter kq.
-template <bool XT>
-__device__ __forceinline__ int slab_group(int kq, int q) {
-    return XT ? 8 * (q >> 1) + 2 * kq + (q & 1) : 8 * kq + q;
-}
+__device__ __forceinline__ int slab_group(int kq, int q) { return 8 * kq + q; }
 
 // Decodes the 8 groups of a code chunk into matrix-core A operands (fp16) and
 // accumulates their products with the activation operands bx into acc.
@@ -125,14 +129,19 @@ __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restr
 }
 
 // The product for one layer, run by workgroup bid of the nwg that serve it.
-// XT: the transposed k order (batch 8 and up).
-template <int SCHEME, int REPL, bool VEC, int RTP, bool XT>
+// XM: how x reaches the registers (XMode).
+template <int SCHEME, int REPL, bool VEC, int RTP, int XM>
 __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, const f16* __restrict__ codebooks,
                                           const f16* __restrict__ scales, f16* __restrict__ y, const int out,
                                           const int bid, const int nwg, const f16* __restrict__ x, int in, int T) {
 
+    constexpr bool XS = XM == kXStaged8 || XM == kXStaged16;
+    constexpr int kStage = kXStageSlots(XM);    // 16-byte slots of one wave's x stage
+    constexpr int kStageRows = kStage / kSlabGroups;
     extern __shared__ u32x4 smem[];
     constexpr int kCbSlots = (SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0;
+    // The per-wave partial tiles; with staged x they share the first stages,
+    // which are idle whenever the tiles are summed.
     float* red = reinterpret_cast<float*>(smem + kCbSlots);
 
     const int tid = threadIdx.x;
@@ -162,14 +171,62 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
     auto load_x = [&](int s) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int grp = s * kSlabGroups + slab_group<XT>(kq, q);
+            const int grp = s * kSlabGroups + slab_group(kq, q);
             bx[q] = (lrow < T && grp < G)
                         ? as_f16x8(load16(x + (size_t)lrow * in + (size_t)grp * kGroup))
                         : f16x8{};
         }
     };
-    load_x(s0);
-    int s_loaded = s0;   // slab whose activations are in bx
+    // Staged x: batch row b, group c of the slab sits in slot kSlabGroups * b + (c ^ b)
+    // of the wave's stage, so the 16 lanes that read one group for 16 rows hit 16
+    // distinct bank groups.  Load i fills slots 64 i .. 64 i + 63 (rows 2i, 2i + 1)
+    // and is issued only if row 2i is in the batch; a row 2i + 1 past the batch
+    // repeats row 2i, a group past the matrix the row's last group.  Every read
+    // stays in x.  Stage rows past the batch keep stale values: a matrix-core
+    // column depends on its own B column only, and the columns past the batch
+    // are discarded; groups past the matrix are zeroed when read.
+    u32x4* const xst = smem + kCbSlots + (XS ? wave * kStage : 0);
+    auto stage_x = [&](int s) {
+        // The lane index passes through an empty asm statement so that the
+        // address arithmetic stays here instead of being hoisted out of the
+        // loops as eight live 64-bit pointers.
+        int l = lane;
+        asm volatile("" : "+v"(l));
+#pragma unroll
+        for (int i = 0; i < kStageRows / 2; ++i) {
+            if (2 * i >= T) break;   // rows past the batch only feed discarded columns
+            const int b = 2 * i + (l >> 5);
+            const int grp = min(s * kSlabGroups + ((l & 31) ^ b), G - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)min(b, T - 1) * in + (size_t)grp * kGroup),
+                                             lds_ptr(xst + 64 * i), 16, 0, 0);
+        }
+    };
+    // Waits for every load of this wave (the stage among them), reads the operand
+    // layout; groups past the end of the row read as zero so that their
+    // products stay zero whatever x holds.
+    auto read_x = [&](int s) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        asm volatile("" ::: "memory");
+        const int b = lrow & (kStageRows - 1);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int c = slab_group(kq, q);
+            const f16x8 v = as_f16x8(xst[kSlabGroups * b + (c ^ b)]);
+            bx[q] = (s * kSlabGroups + c < G) ? v : f16x8{};
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the stage is free again
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int s_loaded = -1;   // slab whose activations are in bx
+    if constexpr (XS) {
+        if (s0 < n_slab) stage_x(s0);
+    } else {
+        load_x(s0);
+        s_loaded = s0;
+    }
 
     // 1x16: warm this XCD's L2 with a 32 KB slice of the codebook (workgroups
     // are dealt to the 8 XCDs round-robin, so 32 consecutive workgroups of one
@@ -209,7 +266,14 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
         for (int s = s0; s < n_slab; s += kGemvWaves) {
             u32x4 ccur[RTP];
 #pragma unroll
-            for (int i = 0; i < RTP; ++i) ccur[i] = XT ? transpose_rows4(cnext[i]) : cnext[i];
+            for (int i = 0; i < RTP; ++i) ccur[i] = cnext[i];
+            if constexpr (XS) {
+                if (s != s_loaded) {
+                    if (s_loaded >= 0) stage_x(s);   // the first slab was staged before the codebook
+                    read_x(s);
+                    s_loaded = s;
+                }
+            }
             // Prefetch the codes of this wave's next slab (or of the next pass).
             {
                 int sn = s + kGemvWaves, rtn = rt0;
@@ -222,11 +286,13 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
                                    : u32x4{0u, 0u, 0u, 0u};
                 }
             }
-            if (s != s_loaded) { load_x(s); s_loaded = s; }
+            if constexpr (!XS) {
+                if (s != s_loaded) { load_x(s); s_loaded = s; }
+            }
             uint32_t gmask = 0u;   // bit q: the group of product q is inside the row
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-                gmask |= (s * kSlabGroups + slab_group<XT>(kq, q) < G) ? (1u << q) : 0u;
+                gmask |= (s * kSlabGroups + slab_group(kq, q) < G) ? (1u << q) : 0u;
 #pragma unroll
             for (int i = 0; i < RTP; ++i) {
                 const int rt = rt0 + i * nwg;
@@ -256,24 +322,29 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
                 }
             }
         }
+        // Staged x, several slabs per wave: the next pass stages its first slab
+        // over the tiles just summed.
+        if constexpr (XS) {
+            if (n_slab > kGemvWaves) __syncthreads();
+        }
     }
     // Keeps the L2 warm-up loads alive; the condition never holds (tid < 1024).
     if ((warm[0] ^ warm[3]) == 0x9e3779b9u && tid == 0xffff) y[0] = (f16)0.f;
 }
 
 // One layer: its arguments directly (a small argument block, read in one round trip).
-template <int SCHEME, int REPL, bool VEC, int RTP, bool XT>
+template <int SCHEME, int REPL, bool VEC, int RTP, int XM>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t* __restrict__ codes,
                                                             const f16* __restrict__ codebooks,
                                                             const f16* __restrict__ scales, f16* __restrict__ y,
                                                             int out, const f16* __restrict__ x, int in, int T) {
-    gemv_body<SCHEME, REPL, VEC, RTP, XT>(codes, codebooks, scales, y, out, (int)blockIdx.x, (int)gridDim.x, x, in, T);
+    gemv_body<SCHEME, REPL, VEC, RTP, XM>(codes, codebooks, scales, y, out, (int)blockIdx.x, (int)gridDim.x, x, in, T);
 }
 
 // Several layers that share x: the workgroup's layer is the number of layer ends at
 // or below blockIdx.x; its first and last workgroups are picked from the ends
 // already in scalar registers.
-template <int SCHEME, int REPL, bool VEC, int RTP, bool XT>
+template <int SCHEME, int REPL, bool VEC, int RTP, int XM>
 __global__ __launch_bounds__(kGemvThreads) void gemv_fused_kernel(const GemvLayers L, const f16* __restrict__ x,
                                                                   int in, int T) {
     int li = 0, wg0 = 0, wg1 = L.wg_end[0];
@@ -284,28 +355,29 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_fused_kernel(const GemvLaye
         wg0 = past ? L.wg_end[i] : wg0;
         wg1 = past ? L.wg_end[i + 1] : wg1;
     }
-    gemv_body<SCHEME, REPL, VEC, RTP, XT>(static_cast<const uint8_t*>(L.codes[li]),
+    gemv_body<SCHEME, REPL, VEC, RTP, XM>(static_cast<const uint8_t*>(L.codes[li]),
                                       static_cast<const f16*>(L.codebooks[li]),
                                       static_cast<const f16*>(L.scales[li]), static_cast<f16*>(L.y[li]), L.out[li],
                                       (int)blockIdx.x - wg0, wg1 - wg0, x, in, T);
 }
 
-template <int SCHEME, int REPL, bool VEC, int RTP, bool XT>
+template <int SCHEME, int REPL, bool VEC, int RTP, int XM>
 static hipError_t launch_gemv_t(const GemvLayers& layers, const void* x, int in, int T, hipStream_t stream) {
     const bool fused = layers.n > 1;
-    const void* kern = fused ? (const void*)gemv_fused_kernel<SCHEME, REPL, VEC, RTP, XT>
-                             : (const void*)gemv_kernel<SCHEME, REPL, VEC, RTP, XT>;
+    const void* kern = fused ? (const void*)gemv_fused_kernel<SCHEME, REPL, VEC, RTP, XM>
+                             : (const void*)gemv_kernel<SCHEME, REPL, VEC, RTP, XM>;
     const size_t lds = (size_t)((SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0) * 16 +
-                       (size_t)kGemvWaves * kRedFloats * sizeof(float);
+                       std::max((size_t)kGemvWaves * kRedFloats * sizeof(float),
+                                (size_t)kGemvWaves * kXStageSlots(XM) * 16);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     if (fused)
-        hipLaunchKernelGGL((gemv_fused_kernel<SCHEME, REPL, VEC, RTP, XT>), dim3(layers.wg_end[layers.n - 1]),
+        hipLaunchKernelGGL((gemv_fused_kernel<SCHEME, REPL, VEC, RTP, XM>), dim3(layers.wg_end[layers.n - 1]),
                            dim3(kGemvThreads), lds, stream, layers, (const f16*)x, in, T);
     else
-        hipLaunchKernelGGL((gemv_kernel<SCHEME, REPL, VEC, RTP, XT>), dim3(layers.wg_end[0]), dim3(kGemvThreads), lds,
+        hipLaunchKernelGGL((gemv_kernel<SCHEME, REPL, VEC, RTP, XM>), dim3(layers.wg_end[0]), dim3(kGemvThreads), lds,
                            stream, static_cast<const uint8_t*>(layers.codes[0]),
                            static_cast<const f16*>(layers.codebooks[0]), static_cast<const f16*>(layers.scales[0]),
                            static_cast<f16*>(layers.y[0]), layers.out[0], (const f16*)x, in, T);
@@ -344,18 +416,31 @@ static void deal_workgroups(GemvLayers& layers, int cus) {
     }
 }
 
-// Below this batch the stored k order is kept; from it up the lanes transpose
-// their code words so that each x load touches one line per batch row.
-constexpr int kGemvTransposeBatch = 8;
+template <int SCHEME, int REPL, int RTP, int XM>
+static hipError_t launch_gemv_v(const GemvLayers& layers, const void* x, int n, int T, hipStream_t stream) {
+    return (n % 64) == 0   // 16-byte aligned code rows
+               ? launch_gemv_t<SCHEME, REPL, true, RTP, XM>(layers, x, n, T, stream)
+               : launch_gemv_t<SCHEME, REPL, false, RTP, XM>(layers, x, n, T, stream);
+}
 
-template <int SCHEME, int REPL, int RTP>
-static hipError_t launch_gemv_s(const GemvLayers& layers, const void* x, int n, int T, hipStream_t stream) {
-    const bool vec = (n % 64) == 0;   // 16-byte aligned code rows
-    if (T >= kGemvTransposeBatch)
-        return vec ? launch_gemv_t<SCHEME, REPL, true, RTP, true>(layers, x, n, T, stream)
-                   : launch_gemv_t<SCHEME, REPL, false, RTP, true>(layers, x, n, T, stream);
-    return vec ? launch_gemv_t<SCHEME, REPL, true, RTP, false>(layers, x, n, T, stream)
-               : launch_gemv_t<SCHEME, REPL, false, RTP, false>(layers, x, n, T, stream);
+// Up to this batch the 2x8 product loads x directly (a few active lanes per
+// load); above it x is staged.
+constexpr int kGemvDirectBatch2x8 = 2;
+// Above this batch the stage holds 16 rows; the 2x8 codebooks then keep 4
+// replicas instead of 8 (LDS: 32 + 128 KB).
+constexpr int kGemvStage8Batch = 8;
+
+template <int RTP>
+static hipError_t launch_gemv_2x8(const GemvLayers& layers, const void* x, int n, int T, hipStream_t stream) {
+    if (T <= kGemvDirectBatch2x8) return launch_gemv_v<kScheme2x8, 8, RTP, kXDirect>(layers, x, n, T, stream);
+    if (T <= kGemvStage8Batch) return launch_gemv_v<kScheme2x8, 8, RTP, kXStaged8>(layers, x, n, T, stream);
+    return launch_gemv_v<kScheme2x8, 4, RTP, kXStaged16>(layers, x, n, T, stream);
+}
+
+template <int RTP>
+static hipError_t launch_gemv_1x16(const GemvLayers& layers, const void* x, int n, int T, hipStream_t stream) {
+    if (T <= kGemvStage8Batch) return launch_gemv_v<kScheme1x16, 1, RTP, kXStaged8>(layers, x, n, T, stream);
+    return launch_gemv_v<kScheme1x16, 1, RTP, kXStaged16>(layers, x, n, T, stream);
 }
 
 hipError_t launch_gemv_fused(int scheme, GemvLayers layers, const void* x, int64_t in,
@@ -364,8 +449,8 @@ hipError_t launch_gemv_fused(int scheme, GemvLayers layers, const void* x, int64
     if (layers.n < 1) return hipSuccess;
     deal_workgroups(layers, device_cu_count());
     const int n = (int)in, T = (int)batch;
-    if (scheme == kScheme2x8) return launch_gemv_s<kScheme2x8, 8, RTP>(layers, x, n, T, stream);
-    return launch_gemv_s<kScheme1x16, 1, RTP>(layers, x, n, T, stream);
+    if (scheme == kScheme2x8) return launch_gemv_2x8<RTP>(layers, x, n, T, stream);
+    return launch_gemv_1x16<RTP>(layers, x, n, T, stream);
 }
 
 hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, const void* scales,

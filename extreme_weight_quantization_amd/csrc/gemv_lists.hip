@@ -51,19 +51,13 @@ constexpr int kListThreads = 1024;
 constexpr int kListWaves = kListThreads / kWave;
 constexpr int kListRing = 8;                     // entry loads per lane and chunk of steps
 constexpr int kListLongPart = 64;
-// s_waitcnt vmcnt(0) lgkmcnt(0), export counter at its maximum; OR a count below
-// 16 into the low bits for vmcnt(count).  Written as the builtin, not as inline
-// assembly, so that the compiler's own wait placement knows what has landed
-// (otherwise it assumes the direct-to-LDS fill may still be in flight and waits
-// for every load at the top of each product loop).
-constexpr int kWaitVm0Lgkm0 = 7 << 4;
+// The prologue waits are written as the builtin, not as inline assembly, so that
+// the compiler's own wait placement knows what has landed (otherwise it assumes
+// the direct-to-LDS fill may still be in flight and waits for every load at the
+// top of each product loop).
 static_assert(kListRing < 16, "vmcnt field");                // launches whose parts have this many steps use two rings
 constexpr int kWgPerSlice = 32;                  // workgroups per (slice, block): 256 in all
 constexpr int kReduceParts = 4;                  // threads per row in the partial sum
-
-__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
-    return (__attribute__((address_space(3))) void*)p;
-}
 
 // 8 fp16 weights times 8 fp16 activations, accumulated in fp32 two products
 // at a time (v_dot2_f32_f16, no rounding between the two products).
@@ -316,7 +310,7 @@ __device__ __forceinline__ void lists_product(const uint32_t* __restrict__ table
     }
     if constexpr (LONG) {
         if (first.n > 0) prefetch_long(first);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0 | 0);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
         __builtin_amdgcn_s_barrier();
         if (first.rt >= 0) run_long(first, wave);
         for (int uu = wave + kListWaves; uu < n_units; uu += kListWaves) {   // only when R > 16 (then P = 1)
@@ -335,7 +329,7 @@ __device__ __forceinline__ void lists_product(const uint32_t* __restrict__ table
 #pragma unroll
         for (int i = 0; i < kListRing; ++i)
             ra[i] = *(any ? first.e + (size_t)(first.t0 + min(i, first.n - 1)) * 64 : stand_in);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0 | kListRing);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kListRing));
         __builtin_amdgcn_s_barrier();
         if (first.rt >= 0) run_short(first, wave);
         for (int uu = wave + kListWaves; uu < n_units; uu += kListWaves) {

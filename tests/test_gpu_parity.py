@@ -140,8 +140,9 @@ def run_gemv(layer):
     (300, 2048, 7),
     (16, 16384, 2),     # wide row: many slabs per wave
     (4096 + 8, 256, 4), # many row tiles per workgroup
-    (100, 520, 12),     # batch 8 and up (transposed k order): ragged rows, unaligned code rows
-    (72, 4104, 8),      # the same at the threshold batch, a partial last slab
+    (100, 520, 12),     # 16-row x stage: ragged rows, unaligned code rows
+    (72, 4104, 8),      # 8-row x stage at its largest batch, a partial last slab
+    (72, 4104, 9),      # 16-row x stage at its smallest batch
     (33, 4160, 16),     # aligned code rows, partial last slab, ragged row tile
 ])
 def test_gemv_small(scheme, out, n_in, batch):
@@ -149,6 +150,34 @@ def test_gemv_small(scheme, out, n_in, batch):
     y = run_gemv(L)
     y_ref = O.linear_ref_f64(L.codes, L.codebooks, L.scales, L.x)
     assert_close(y, y_ref, f"{scheme} {out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("scheme", ["2x8", "1x16"])
+@pytest.mark.parametrize("batch", [3, 16])
+def test_gemv_several_passes_and_slabs(scheme, batch):
+    """8200 rows: workgroups run a second pass of row tiles, and 545 groups make
+    two slabs for some waves, so a pass re-stages x after the previous pass's
+    partial tiles were summed in the same LDS."""
+    L = synth.make_layer(scheme, 8200, 4360, batch=batch, seed=batch)
+    y = run_gemv(L)
+    rows = np.unique(np.concatenate([sample_rows(8200, 48), np.arange(8184, 8200), np.arange(4096, 4112)]))
+    assert_close(y[:, rows], O.linear_ref_rows_f64(L.codes, L.codebooks, L.scales, L.x, rows), f"{scheme} b{batch}")
+
+
+@pytest.mark.parametrize("scheme", ["2x8", "1x16"])
+@pytest.mark.parametrize("big,small", [(8, 3), (16, 9)])
+def test_gemv_stale_stage_rows_do_not_leak(scheme, big, small):
+    """A call at a larger batch leaves NaN in the LDS rows of x that a following
+    call at a smaller batch does not load; its outputs stay finite and right."""
+    L = synth.make_layer(scheme, 512, 2048, batch=big, seed=7)
+    L.x[small:] = np.nan
+    codes, cb, s, x = dev(L)
+    y_big = E.aqlm_linear_gemv(codes, cb, s, x)
+    y = E.aqlm_linear_gemv(codes, cb, s, x[:small].contiguous()).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    assert torch.isnan(y_big[small:]).all()
+    assert np.isfinite(y).all()
+    assert_close(y, O.linear_ref_f64(L.codes, L.codebooks, L.scales, L.x[:small]), f"{scheme} b{small} after b{big}")
 
 
 @pytest.mark.parametrize("scheme", ["2x8", "1x16"])
@@ -237,6 +266,7 @@ def run_fused(layers, x):
 @pytest.mark.parametrize("outs,n_in,batch", [
     ((4096, 4096, 4096), 4096, 1),        # q, k, v of a 7B attention block
     ((4096, 4096, 4096), 4096, 16),
+    ((4096,) * 4, 11008, 16),             # 64 workgroups a layer: two passes of three slabs a wave
     ((11008, 11008), 4096, 4),            # gate, up of a 7B MLP
     ((100, 4096, 37, 1000), 520, 3),      # ragged rows and in, uneven layers
     ((16,) * 8, 256, 1),                  # the most layers one call takes
