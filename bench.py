@@ -18,7 +18,13 @@ codebook gathers), alone and with q,k,v and gate,up fused; 2x8 GEMV at batch
 1/4/16 on the same block; the Llama-2-70B 1x16 layers at batch 1 in both
 layouts; the 2048-token prefill GEMM on the 7B shapes (both schemes); the
 standalone decode kernel; the other 2-bit schemes; the encoder; and the fp16
-comparator.  The CPU oracle is timed on the host over whole block steps.
+comparator.  Secondary figures: the headline as a share of a measured
+device-to-device copy's bandwidth, the effective weight rate (fp16-equivalent
+weight bytes 2 out in per second: a reading of a term the pages leave
+undefined), and, not counted, the same step with one buffer set reused (codes
+resident in the last-level cache).  The CPU oracle is timed on the host over
+whole block steps, with the CPU model, the BLAS numpy uses and the share of
+its time spent decoding.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 Prints one JSON line on stdout.
@@ -26,6 +32,7 @@ Prints one JSON line on stdout.
 from __future__ import annotations
 
 import argparse
+import copy
 import json
 import os
 import sys
@@ -246,6 +253,25 @@ def time_gemv(torch, E, ls: LayerSet, steps, warmup, lists=False):
     return ms_step, per_shape
 
 
+def hbm_copy_gbps(torch, mib=512, reps=10):
+    """Read + write bytes per second of a plain device-to-device copy (the measured
+    streaming bandwidth the GEMV rates are also compared with)."""
+    src = torch.empty(mib << 19, dtype=torch.float16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    gbps = 2 * (mib << 20) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
 def time_calls(torch, launch, iters, warmup):
     """Mean us per launch of `launch(i)` over `iters` back-to-back launches in a HIP graph."""
     for i in range(warmup):
@@ -323,12 +349,32 @@ def cpu_baseline(min_seconds=10.0):
             elapsed += time.perf_counter() - t
             nbytes += gemv_bytes(shape[0], shape[1], 1)
         steps += 1
+    # the oracle's fp32 decode alone, once per layer of a step (the rest of its time is the product)
+    dec = 0.0
+    for shape in BLOCK_7B:
+        L = layers[shape]
+        t = time.perf_counter()
+        O.decode_fp32(L.codes, L.codebooks, L.scales)
+        dec += time.perf_counter() - t
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
+    blas = None
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]["name"]
+    except Exception:  # pragma: no cover
+        pass
     return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"numpy oracle (fp32 decode + float64 product) on {steps} Llama-2-7B block steps "
                       f"(7 AQLM 1x16 layers each, batch 1): {elapsed:.1f} s for {nbytes / 1e6:.1f} MB "
                       "counted bytes",
-            "us_per_layer": round(elapsed / (7 * steps) * 1e6, 1)}
+            "us_per_layer": round(elapsed / (7 * steps) * 1e6, 1),
+            "decode_share": round(dec / (elapsed / steps), 3),
+            "cpu_model": cpu_model, "blas": blas}
 
 
 def main():
@@ -368,13 +414,25 @@ def main():
 
     def shape_table(su, batch=1):
         return {f"{o}x{i}": {"us": round(us, 3), "GBps": round(gemv_bytes(o, i, batch) / (us * 1e-6) / 1e9, 1),
-                             "pct_hbm_peak": round(100 * gemv_bytes(o, i, batch) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+                             "pct_hbm_peak": round(100 * gemv_bytes(o, i, batch) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                             "effective_weight_GBps": round(2 * o * i / (us * 1e-6) / 1e9, 1)}
                 for (o, i), us in su.items()}
 
     per_shape = shape_table(shape_us)
     breakdown = {"gemv_1x16_b1_7b": per_shape}
+    copy_gbps = hbm_copy_gbps(torch)
+    breakdown["hbm_copy"] = {"GBps": round(copy_gbps, 1),
+                             "what": "torch device-to-device copy of 512 MiB, read + write bytes per second"}
     fused = {}
     if not args.quick:
+        # not counted: one buffer set reused every step, so the codes stay in the last-level cache
+        hot = copy.copy(ls)
+        hot.sets, hot.lists = ls.sets[:1], ls.lists[:1]
+        ms_hot, _ = time_gemv(torch, E, hot, args.steps, args.warmup, lists=True)
+        breakdown["gemv_1x16_b1_7b_hot_single_set"] = {
+            "ms_per_step": round(ms_hot, 5), "GBps_step": round(ls.bytes_per_step / (ms_hot * 1e-3) / 1e9, 1),
+            "note": "not counted: the same buffers every step (resident in the 256 MB last-level cache)"}
+        del hot
         # the same layers and buffers with the codes in their stored layout (per-code L2 gathers)
         worst_plain = spot_check(torch, E, ls)
         ms_plain, shape_plain = time_gemv(torch, E, ls, args.steps, args.warmup)
@@ -587,6 +645,8 @@ def main():
             "rotated_buffer_sets": n_sets, "parallelism": "single GPU",
             "us_per_layer": round(ms_step * 1e3 / len(BLOCK_7B), 3),
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "pct_measured_copy_bw": round(100 * value / copy_gbps, 2),
+            "effective_weight_GBps": round(sum(2 * o * i for o, i in BLOCK_7B) / (ms_step * 1e-3) / 1e9, 1),
             "spot_check_rel_l2": worst,
             "device": dev_name,
         },
