@@ -545,10 +545,16 @@ def main():
             w = torch.empty((4096, 4096), dtype=torch.float16, device="cuda")
             x1 = make_x(torch, 1, 4096, gen)
             y1 = torch.empty((1, 4096), dtype=torch.float16, device="cuda")
+            x16 = make_x(torch, 16, 4096, gen)
+            y16 = torch.empty((16, 4096), dtype=torch.float16, device="cuda")
             x2 = make_x(torch, 2048, 4096, gen)
             y2 = torch.empty((2048, 4096), dtype=torch.float16, device="cuda")
             us_d = time_calls(torch, lambda i: E.aqlm_linear_decode(codes, cbg, s, w), 20, 3)
-            us_v = time_calls(torch, lambda i: E.aqlm_linear_gemv(codes, cbg, s, x1, y1), 50, 3)
+            # GEMV: 64 code sets (270 MB) in turn, so that no set is still in the last-level cache
+            cset = [codes] + [make_generic(torch, M, B, g, 4096, 4096, gen)[1] for _ in range(63)]
+            us_v = time_calls(torch, lambda i: E.aqlm_linear_gemv(cset[i % 64], cbg, s, x1, y1), 128, 3)
+            us_v16 = time_calls(torch, lambda i: E.aqlm_linear_gemv(cset[i % 64], cbg, s, x16, y16), 128, 3)
+            del cset
             us_m = time_calls(torch, lambda i: E.aqlm_linear_gemm(codes, cbg, s, x2, y2), 5, 1)
             wsg = torch.empty((E.gemm_dequant_workspace_bytes(M, B, g, 4096, 4096),), dtype=torch.uint8,
                               device="cuda")
@@ -558,12 +564,14 @@ def main():
             gs[f"{M}x{B}g{g}_4096x4096"] = {
                 "decode_us": round(us_d, 2), "decode_GBps": round(dbytes / (us_d * 1e-6) / 1e9, 1),
                 "gemv_b1_us": round(us_v, 2), "gemv_b1_GBps": round(nb / (us_v * 1e-6) / 1e9, 1),
+                "gemv_b16_us": round(us_v16, 2),
+                "gemv_b16_GBps": round(generic_gemv_bytes(M, B, g, 4096, 4096, 16) / (us_v16 * 1e-6) / 1e9, 1),
                 "gemm_2048_us": round(us_m, 1),
                 "gemm_2048_frac_mfma_peak": round(2.0 * 2048 * 4096 * 4096 / (us_m * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
                 "gemm_2048_two_pass_us": round(us_m2, 1),
                 "gemm_2048_two_pass_frac_mfma_peak": round(
                     2.0 * 2048 * 4096 * 4096 / (us_m2 * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
-            del cbg, codes, s, w, x1, y1, x2, y2, wsg
+            del cbg, codes, s, w, x1, y1, x16, y16, x2, y2, wsg
             torch.cuda.empty_cache()
         breakdown["generic_schemes"] = gs
         # greedy residual encoder and residual k-means (3 unfused fp32 ops per codeword entry compared)

@@ -40,6 +40,19 @@ static bool generic_scheme_ok(int M, int B, int g) {
            (g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32);
 }
 
+// The GEMV of the other 2-bit schemes with B = 8 (g = 4 M) runs the 2x8 product's
+// kernel, which reads 2 bytes of codes per 8 inputs (in % 8 == 0): 1x8 g4 and 4x8 g16
+// at every batch, 8x8 g32 above batch 8 (below, where its eight lookups per 8 inputs
+// and single codebook copy dominate, the general kernel was faster).  -1: the
+// general kernel.
+static int gemv_b8_scheme(int M, int B, int g, int64_t in, int64_t batch) {
+    if (B != 8 || g != 4 * M || in % 8 != 0) return -1;
+    if (M == 1) return kSchemeB8M1;
+    if (M == 4) return kSchemeB8M4;
+    if (M == 8 && batch > 8) return kSchemeB8M8;
+    return -1;
+}
+
 // Host-side validation shared by the entry points.  Returns AQLM_OK and the
 // scheme id, or an error status; touches no HIP state.
 static int validate(Op op, const void* codes, const void* codebooks, const void* scales,
@@ -91,6 +104,7 @@ int aqlm_linear_gemv(const void* codes, const void* codebooks, const void* scale
     bool empty = false;
     const int st = validate(Op::kGemv, codes, codebooks, scales, x, y, M, B, g, out, in, batch, &scheme, &empty);
     if (st != AQLM_OK || empty) return st;
+    if (scheme == kSchemeGeneric && gemv_b8_scheme(M, B, g, in, batch) >= 0) scheme = gemv_b8_scheme(M, B, g, in, batch);
     if (scheme == kSchemeGeneric)
         return finish(launch_gemv_generic(GenericScheme{M, B, g}, codes, codebooks, scales, x, y, out, in,
                                           batch, (hipStream_t)stream));
@@ -120,6 +134,7 @@ int aqlm_linear_gemv_fused(int n_layers, const void* const* codes, const void* c
         ++layers.n;
     }
     if (layers.n == 0) return AQLM_OK;
+    if (scheme == kSchemeGeneric && gemv_b8_scheme(M, B, g, in, batch) >= 0) scheme = gemv_b8_scheme(M, B, g, in, batch);
     if (scheme == kSchemeGeneric) {   // one launch per layer
         for (int l = 0; l < layers.n; ++l) {
             const int st = finish(launch_gemv_generic(GenericScheme{M, B, g}, layers.codes[l], layers.codebooks[l],

@@ -13,8 +13,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Scheme ids used as template parameters.
-// kSchemeGeneric: any other (M, B, g), served by the kernels of generic.hip
-enum Scheme : int { kScheme2x8 = 0, kScheme1x16 = 1, kSchemeGeneric = 2 };
+// kSchemeGeneric: any other (M, B, g), served by the kernels of generic.hip.
+// kSchemeB8M1/M4/M8: the other 2-bit schemes with B = 8 (1x8 g4, 4x8 g16,
+// 8x8 g32; 2x8 g8 is kScheme2x8), whose GEMV runs the 2x8 product's kernel.
+enum Scheme : int { kScheme2x8 = 0, kScheme1x16 = 1, kSchemeGeneric = 2, kSchemeB8M1 = 3, kSchemeB8M4 = 4,
+                    kSchemeB8M8 = 5 };
+
+// Codebooks of a 2-bit B = 8 scheme (g = 4 M), 0 for the others.
+constexpr int b8_codebooks(int scheme) {
+    return scheme == kScheme2x8 ? 2 : scheme == kSchemeB8M1 ? 1 : scheme == kSchemeB8M4 ? 4
+         : scheme == kSchemeB8M8 ? 8 : 0;
+}
 
 constexpr int kGroup = 8;          // g: inputs per group
 constexpr int kWave = 64;          // CDNA wavefront width

@@ -92,14 +92,78 @@ __device__ __forceinline__ u32x4 load_codes(const uint8_t* __restrict__ codes, i
 // Group of product q (0..7) in the slab for the lane of k-quarter kq.
 __device__ __forceinline__ int slab_group(int kq, int q) { return 8 * kq + q; }
 
-// Decodes the 8 groups of a code chunk into matrix-core A operands (fp16) and
-// accumulates their products with the activation operands bx into acc.
-// Groups past the end of the row (ok mask bit clear) contribute zero.  The
-// lookups of four groups are issued before any of them is consumed.
+// 16-byte LDS slots of the codebooks of a 2-bit B = 8 scheme with REPL
+// replicas: codeword k of codebook m, 8-entry piece h (of H = g / 8) sits in
+// slot ((k M + m) H + h) REPL + r (2x8: (2k + m) REPL + r).  1x8 g4 keeps its
+// 4-entry codewords in 8-byte slots k REPL + r (half as many 16-byte slots).
+// 0 for 1x16.
+template <int SCHEME, int REPL>
+constexpr int cb_slots() {
+    constexpr int M = b8_codebooks(SCHEME);
+    return M == 0 ? 0 : M == 1 ? kCodewords2x8 / 2 * REPL : kCodewords2x8 * M * (M / 2) * REPL;
+}
+
+// Byte b (0..15) of a lane's 16 bytes of codes.
+__device__ __forceinline__ uint32_t code_byte(const u32x4 cv, int b) { return (cv[b >> 2] >> (8 * (b & 3))) & 0xff; }
+
+// Decodes the 8 pieces of 8 inputs that a lane's 16 bytes of codes cover into
+// matrix-core A operands (fp16) and accumulates their products with the
+// activation operands bx into acc.  Pieces past the end of the row (ok mask
+// bit clear) contribute zero.  The lookups of four pieces are issued before
+// any of them is used.
+//   2x8 (g = 8): piece q is group q, two codewords added in fp16 (exact in
+//     fp32, one rounding);
+//   1x16: piece q is group q, its codeword gathered from the L2-resident codebook;
+//   1x8 g4: piece q is groups 2q and 2q+1, one 8-byte codeword each;
+//   4x8 g16 / 8x8 g32: piece q is part q % H of group q / H (H = 2 or 4), the
+//     M codewords' parts added in fp32 from codebook 0 upward, rounded once
+//     (one piece at a time for 8x8, which would otherwise run out of registers).
 template <int SCHEME, int REPL>
 __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restrict__ cb_lds,
                                             const f16* __restrict__ codebooks, int rrep,
                                             uint32_t ok_mask, const f16x8 (&bx)[8], f32x4 acc) {
+    constexpr int M = b8_codebooks(SCHEME);
+    if constexpr (M == 1) {
+        const u32x2* cb8 = reinterpret_cast<const u32x2*>(cb_lds);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f16x8 a[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int p = 4 * h + q;
+                const u32x2 lo = cb8[code_byte(cv, 2 * p) * REPL + rrep];
+                const u32x2 hi = cb8[code_byte(cv, 2 * p + 1) * REPL + rrep];
+                a[q] = as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a[q] = ((ok_mask >> (4 * h + q)) & 1) ? a[q] : f16x8{};
+                acc = mfma16x16x32(a[q], bx[4 * h + q], acc);
+            }
+        }
+        return acc;
+    } else if constexpr (M >= 4) {
+        constexpr int H = M / 2;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int gi = q / H, h = q % H;
+            float sum[8];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint32_t k = code_byte(cv, gi * M + m);
+                const f16x8 c = as_f16x8(cb_lds[((k * M + m) * H + h) * REPL + rrep]);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) sum[t] = m == 0 ? (float)c[t] : sum[t] + (float)c[t];
+            }
+            f16x8 a;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) a[t] = (f16)sum[t];
+            a = ((ok_mask >> q) & 1) ? a : f16x8{};
+            acc = mfma16x16x32(a, bx[q], acc);
+            if constexpr (M == 8) __builtin_amdgcn_sched_barrier(0);
+        }
+        return acc;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         f16x8 a[4];
@@ -139,7 +203,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
     constexpr int kStage = kXStageSlots(XM);    // 16-byte slots of one wave's x stage
     constexpr int kStageRows = kStage / kSlabGroups;
     extern __shared__ u32x4 smem[];
-    constexpr int kCbSlots = (SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0;
+    constexpr int kCbSlots = cb_slots<SCHEME, REPL>();
     // The per-wave partial tiles; with staged x they share the first stages,
     // which are idle whenever the tiles are summed.
     float* red = reinterpret_cast<float*>(smem + kCbSlots);
@@ -238,22 +302,45 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
         warm = load16(cb16 + slice + tid) ^ load16(cb16 + slice + kGemvThreads + tid);
     }
 
-    if constexpr (SCHEME == kScheme2x8) {
-        // Slot j holds entry (m, k) of replica r, j = (2k + m) * REPL + r; consecutive
-        // threads write consecutive slots (conflict-free), reading the same 16 B source.
-        // All loads first (one L2 round trip), then the LDS writes.
-        constexpr int kFill = (kCbSlots + kGemvThreads - 1) / kGemvThreads;
-        u32x4 fv[kFill];
+    constexpr int kM = b8_codebooks(SCHEME);
+    if constexpr (kM == 1) {
+        // 8-byte slot j = k * REPL + r holds codeword k (4 fp16); loads first, then LDS writes
+        constexpr int kSlots8 = 2 * kCbSlots;
+        constexpr int kFill = (kSlots8 + kGemvThreads - 1) / kGemvThreads;
+        u32x2* cb8 = reinterpret_cast<u32x2*>(smem);
+        u32x2 fv[kFill];
 #pragma unroll
         for (int it = 0; it < kFill; ++it) {
-            const int j = min(it * kGemvThreads + tid, kCbSlots - 1);
-            const int km = j / REPL;
-            fv[it] = load16(codebooks + (size_t)((km & 1) * kCodewords2x8 + (km >> 1)) * kGroup);
+            const int j = min(it * kGemvThreads + tid, kSlots8 - 1);
+            fv[it] = *reinterpret_cast<const u32x2*>(codebooks + (size_t)(j / REPL) * 4);
         }
 #pragma unroll
         for (int it = 0; it < kFill; ++it) {
             const int j = it * kGemvThreads + tid;
-            if (j < kCbSlots) smem[j] = fv[it];
+            if (j < kSlots8) cb8[j] = fv[it];
+        }
+    } else if constexpr (kM >= 2) {
+        // Slot j holds piece h of codeword k of codebook m, replica r:
+        // j = ((k M + m) H + h) REPL + r.  Consecutive threads write consecutive slots
+        // (conflict-free), reading the same 16 B source.  Loads first (one L2 round
+        // trip), then the LDS writes, in rounds of at most 4 loads a thread.
+        constexpr int kH = kM / 2, kG = 4 * kM;
+        constexpr int kFill = (kCbSlots + kGemvThreads - 1) / kGemvThreads;
+        constexpr int kRound = kFill < 4 ? kFill : 4;
+#pragma unroll
+        for (int r0 = 0; r0 < kFill; r0 += kRound) {
+            u32x4 fv[kRound];
+#pragma unroll
+            for (int it = 0; it < kRound; ++it) {
+                const int j = min((r0 + it) * kGemvThreads + tid, kCbSlots - 1);
+                const int kmh = j / REPL, km = kmh / kH;
+                fv[it] = load16(codebooks + (size_t)((km % kM) * kCodewords2x8 + km / kM) * kG + (kmh % kH) * 8);
+            }
+#pragma unroll
+            for (int it = 0; it < kRound; ++it) {
+                const int j = (r0 + it) * kGemvThreads + tid;
+                if (j < kCbSlots) smem[j] = fv[it];
+            }
         }
     }
     __syncthreads();
@@ -366,7 +453,7 @@ static hipError_t launch_gemv_t(const GemvLayers& layers, const void* x, int in,
     const bool fused = layers.n > 1;
     const void* kern = fused ? (const void*)gemv_fused_kernel<SCHEME, REPL, VEC, RTP, XM>
                              : (const void*)gemv_kernel<SCHEME, REPL, VEC, RTP, XM>;
-    const size_t lds = (size_t)((SCHEME == kScheme2x8) ? 2 * kCodewords2x8 * REPL : 0) * 16 +
+    const size_t lds = (size_t)cb_slots<SCHEME, REPL>() * 16 +
                        std::max((size_t)kGemvWaves * kRedFloats * sizeof(float),
                                 (size_t)kGemvWaves * kXStageSlots(XM) * 16);
     if (lds > 65536) {
@@ -437,6 +524,26 @@ static hipError_t launch_gemv_2x8(const GemvLayers& layers, const void* x, int n
     return launch_gemv_v<kScheme2x8, 4, RTP, kXStaged16>(layers, x, n, T, stream);
 }
 
+// The other 2-bit B = 8 schemes: as 2x8, with the replicas that fit next to the x stage.
+// 1x8 g4 (2 KB a copy): 8 replicas.  4x8 g16 (32 KB): 2, and 1 with the 16-row stage.
+// 8x8 g32 (128 KB): one copy and direct x loads (no room for a stage); its launcher
+// takes it only above batch 8.
+template <int RTP>
+static hipError_t launch_gemv_b8(int scheme, const GemvLayers& layers, const void* x, int n, int T,
+                                 hipStream_t stream) {
+    if (scheme == kSchemeB8M1) {
+        if (T <= kGemvDirectBatch2x8) return launch_gemv_v<kSchemeB8M1, 8, RTP, kXDirect>(layers, x, n, T, stream);
+        if (T <= kGemvStage8Batch) return launch_gemv_v<kSchemeB8M1, 8, RTP, kXStaged8>(layers, x, n, T, stream);
+        return launch_gemv_v<kSchemeB8M1, 8, RTP, kXStaged16>(layers, x, n, T, stream);
+    }
+    if (scheme == kSchemeB8M4) {
+        if (T <= kGemvDirectBatch2x8) return launch_gemv_v<kSchemeB8M4, 2, RTP, kXDirect>(layers, x, n, T, stream);
+        if (T <= kGemvStage8Batch) return launch_gemv_v<kSchemeB8M4, 2, RTP, kXStaged8>(layers, x, n, T, stream);
+        return launch_gemv_v<kSchemeB8M4, 1, RTP, kXStaged16>(layers, x, n, T, stream);
+    }
+    return launch_gemv_v<kSchemeB8M8, 1, RTP, kXDirect>(layers, x, n, T, stream);
+}
+
 template <int RTP>
 static hipError_t launch_gemv_1x16(const GemvLayers& layers, const void* x, int n, int T, hipStream_t stream) {
     if (T <= kGemvStage8Batch) return launch_gemv_v<kScheme1x16, 1, RTP, kXStaged8>(layers, x, n, T, stream);
@@ -450,7 +557,8 @@ hipError_t launch_gemv_fused(int scheme, GemvLayers layers, const void* x, int64
     deal_workgroups(layers, device_cu_count());
     const int n = (int)in, T = (int)batch;
     if (scheme == kScheme2x8) return launch_gemv_2x8<RTP>(layers, x, n, T, stream);
-    return launch_gemv_1x16<RTP>(layers, x, n, T, stream);
+    if (scheme == kScheme1x16) return launch_gemv_1x16<RTP>(layers, x, n, T, stream);
+    return launch_gemv_b8<RTP>(scheme, layers, x, n, T, stream);
 }
 
 hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, const void* scales,

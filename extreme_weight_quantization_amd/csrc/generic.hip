@@ -9,8 +9,9 @@
 // the low B bits.  Figure 2 of the MCQ section gives the dequantization: the M
 // selected codewords are summed, then scaled by the row's factor.
 //
-// The 1x16 and 2x8 schemes at g = 8 have their own tuned kernels; these serve
-// every other triple:
+// The 1x16 and 2x8 schemes at g = 8 have their own tuned kernels, and the GEMV
+// of the other 2-bit B = 8 schemes (1x8 g4, 4x8 g16; 8x8 g32 above batch 8) runs
+// the 2x8 one when in % 8 == 0; these serve every other case:
 //   decode_generic_kernel : W16 exactly as the 1x16/2x8 decode kernel (fp32 sum
 //                           from codebook 0 upward, fp32 scale, one RNE rounding);
 //   gemv_generic_kernel   : batch 1..16, one wave per row, 16 waves per

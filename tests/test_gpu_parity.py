@@ -404,6 +404,69 @@ def test_generic_gemv(M, B, g, batch):
                  f"gemv {M}x{B}g{g} T{batch}")
 
 
+# The other 2-bit schemes with B = 8 (g = 4 M).  Their GEMV runs the 2x8 kernel when
+# in % 8 == 0 (1x8 g4 and 4x8 g16 at every batch with direct x, 8-row and 16-row stages;
+# 8x8 g32 above batch 8, with direct x), else the general one.
+B8_FAMILY = [(1, 8, 4), (4, 8, 16), (8, 8, 32)]
+
+
+@pytest.mark.parametrize("M,B,g", B8_FAMILY)
+@pytest.mark.parametrize("out,n_in,batch", [
+    (300, 4096, 1),     # direct x loads, one slab per wave
+    (300, 4096, 2),
+    (72, 4160, 3),      # 8-row x stage, partial last slab, aligned code rows
+    (72, 4160, 8),
+    (100, 1056, 9),     # 16-row x stage, unaligned code rows
+    (33, 4160, 16),     # ragged row tile
+    (4104, 512, 4),     # many row tiles per workgroup
+    (16, 16384, 1),     # many slabs per wave
+])
+def test_gemv_b8_family(M, B, g, out, n_in, batch):
+    L = synth.make_layer_mbg(M, B, g, out, n_in, batch=batch, seed=out + batch + M)
+    c, cb, s, x = gdev(L, L.codes)
+    y = E.aqlm_linear_gemv(c, cb, s, x)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy().astype(np.float64), O.linear_ref_f64(L.codes, L.codebooks, L.scales, L.x),
+                 f"gemv {M}x{B}g{g} {out}x{n_in} T{batch}")
+
+
+@pytest.mark.parametrize("M,B,g", B8_FAMILY)
+@pytest.mark.parametrize("shape,batch", [((4096, 11008), 16), ((11008, 4096), 1), ((4096, 4096), 4)])
+def test_gemv_b8_family_7b(M, B, g, shape, batch):
+    out, n_in = shape
+    L = synth.make_layer_mbg(M, B, g, out, n_in, batch=batch, seed=M)
+    c, cb, s, x = gdev(L, L.codes)
+    y = E.aqlm_linear_gemv(c, cb, s, x).cpu().numpy().astype(np.float64)
+    rows = sample_rows(out, 48)
+    assert_close(y[:, rows], O.linear_ref_rows_f64(L.codes, L.codebooks, L.scales, L.x, rows),
+                 f"gemv {M}x{B}g{g} {shape} T{batch}")
+
+
+def test_gemv_1x8g4_unaligned_in_runs_the_general_kernel():
+    """in % 8 != 0 (in = 4 * odd): 1x8 g4 falls back to the general kernel."""
+    L = synth.make_layer_mbg(1, 8, 4, 200, 4 * 1027, batch=3, seed=11)
+    c, cb, s, x = gdev(L, L.codes)
+    y = E.aqlm_linear_gemv(c, cb, s, x).cpu().numpy().astype(np.float64)
+    assert_close(y, O.linear_ref_f64(L.codes, L.codebooks, L.scales, L.x), "1x8g4 in=4108")
+
+
+@pytest.mark.parametrize("M,B,g", B8_FAMILY)
+@pytest.mark.parametrize("batch", [5, 16])
+def test_gemv_b8_family_fused(M, B, g, batch):
+    """The fused entry point (one launch, or one per layer on the general kernel) equals separate calls."""
+    layers = [synth.make_layer_mbg(M, B, g, o, 2048, batch=batch, seed=20 + i) for i, o in enumerate((300, 4096, 100))]
+    xd = torch.from_numpy(layers[0].x).cuda()
+    dl = [gdev(L, L.codes)[:3] for L in layers]
+    ys = E.aqlm_linear_gemv_fused(dl, xd)
+    sep = [E.aqlm_linear_gemv(c, cb, s, xd) for (c, cb, s) in dl]
+    torch.cuda.synchronize()
+    for i, (L, yf, ys1) in enumerate(zip(layers, ys, sep)):
+        np.testing.assert_array_equal(yf.cpu().numpy().view(np.uint16), ys1.cpu().numpy().view(np.uint16))
+        rows = sample_rows(L.codes.shape[0], 32)
+        assert_close(yf.cpu().numpy().astype(np.float64)[:, rows],
+                     O.linear_ref_rows_f64(L.codes, L.codebooks, L.scales, layers[0].x, rows), f"fused layer {i}")
+
+
 @pytest.mark.parametrize("M,B,g", GENERIC)
 @pytest.mark.parametrize("out,n_grp,batch", [(200, 37, 130), (64, 8, 3)])
 def test_generic_gemm(M, B, g, out, n_grp, batch):
