@@ -321,27 +321,21 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
         }
     } else if constexpr (kM >= 2) {
         // Slot j holds piece h of codeword k of codebook m, replica r:
-        // j = ((k M + m) H + h) REPL + r.  Consecutive threads write consecutive slots
-        // (conflict-free), reading the same 16 B source.  Loads first (one L2 round
-        // trip), then the LDS writes, in rounds of at most 4 loads a thread.
+        // j = ((k M + m) H + h) REPL + r.  Direct-to-LDS loads: load it of wave w fills
+        // slots it * 1024 + 64 w .. + 63, lane l slot it * 1024 + 64 w + l, from the 16 B
+        // of its piece; then every load of the wave is waited for (the code and x
+        // loads issued before it too).
         constexpr int kH = kM / 2, kG = 4 * kM;
-        constexpr int kFill = (kCbSlots + kGemvThreads - 1) / kGemvThreads;
-        constexpr int kRound = kFill < 4 ? kFill : 4;
+        static_assert(kCbSlots % kGemvThreads == 0, "whole waves of slots");
 #pragma unroll
-        for (int r0 = 0; r0 < kFill; r0 += kRound) {
-            u32x4 fv[kRound];
-#pragma unroll
-            for (int it = 0; it < kRound; ++it) {
-                const int j = min((r0 + it) * kGemvThreads + tid, kCbSlots - 1);
-                const int kmh = j / REPL, km = kmh / kH;
-                fv[it] = load16(codebooks + (size_t)((km % kM) * kCodewords2x8 + km / kM) * kG + (kmh % kH) * 8);
-            }
-#pragma unroll
-            for (int it = 0; it < kRound; ++it) {
-                const int j = (r0 + it) * kGemvThreads + tid;
-                if (j < kCbSlots) smem[j] = fv[it];
-            }
+        for (int it = 0; it < kCbSlots / kGemvThreads; ++it) {
+            const int j = it * kGemvThreads + tid;
+            const int kmh = j / REPL, km = kmh / kH;
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(codebooks + (size_t)((km % kM) * kCodewords2x8 + km / kM) * kG + (kmh % kH) * 8),
+                lds_ptr(smem + it * kGemvThreads + wave * 64), 16, 0, 0);
         }
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     }
     __syncthreads();
 
