@@ -13,7 +13,9 @@
 // of the other 2-bit B = 8 schemes (1x8 g4, 4x8 g16; 8x8 g32 above batch 8) runs
 // the 2x8 one when in % 8 == 0; these serve every other case:
 //   decode_generic_kernel : W16 exactly as the 1x16/2x8 decode kernel (fp32 sum
-//                           from codebook 0 upward, fp32 scale, one RNE rounding);
+//                           from codebook 0 upward, fp32 scale, one RNE rounding),
+//                           16-byte stores (for g < 8 and in % 8 == 0, 8/g
+//                           groups a thread);
 //   gemv_generic_kernel   : batch 1..16, one wave per row, 16 waves per
 //                           workgroup, fp32 weights;
 //   gemm_generic_kernel   : any batch, 128x128 tiles, W decoded into LDS in
@@ -106,14 +108,16 @@ __device__ __forceinline__ void stage_codebook(f16* dst, const f16* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Decode: one thread per group, bit-exact.  LDS: codebooks of at most
-// kGemvLdsCodebook bytes are copied to LDS first (1024-thread workgroups), so the
-// lookups are LDS reads instead of L2 gathers.
-template <int G, int CB, bool LDS>
+// Decode: one thread per KG consecutive groups, bit-exact.  KG = 1, or 8 / G for
+// G < 8 when a row holds a whole number of 8-input pieces (in % 8 == 0): then the
+// KG groups lie in one row and leave as one 16-byte store.  LDS: codebooks of at
+// most kGemvLdsCodebook bytes are copied to LDS first (1024-thread workgroups),
+// so the lookups are LDS reads instead of L2 gathers.
+template <int G, int CB, bool LDS, int KG>
 __global__ __launch_bounds__(1024) void decode_generic_kernel(const uint8_t* __restrict__ codes,
                                                               const f16* __restrict__ codebooks,
                                                               const f16* __restrict__ scales,
-                                                              f16* __restrict__ w, uint32_t n_groups,
+                                                              f16* __restrict__ w, uint32_t n_units,
                                                               uint32_t n_grp_row, int M, int B) {
     extern __shared__ u32x4 smem[];
     const f16* cb = codebooks;
@@ -124,7 +128,23 @@ __global__ __launch_bounds__(1024) void decode_generic_kernel(const uint8_t* __r
     }
     const uint32_t mask = (1u << B) - 1u;
     const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x; gid < n_groups; gid += stride) {
+    for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < n_units; u += stride) {
+        if constexpr (KG > 1) {
+            static_assert(G * KG == 8, "one 16-byte store per unit");
+            const uint32_t gid0 = u * KG;
+            const float s = (float)scales[gid0 / n_grp_row];
+            f16x8 o;
+#pragma unroll
+            for (int k = 0; k < KG; ++k) {
+                float v[G];
+                group_weights<G, CB>(codes, (size_t)(gid0 + k) * M, cb, M, B, mask, v);
+#pragma unroll
+                for (int t = 0; t < G; ++t) o[k * G + t] = (f16)__fmul_rn(v[t], s);
+            }
+            __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(w + (size_t)gid0 * G));
+            continue;
+        }
+        const uint32_t gid = u;
         const float s = (float)scales[gid / n_grp_row];
         float v[G];
         group_weights<G, CB>(codes, (size_t)gid * M, cb, M, B, mask, v);
@@ -143,9 +163,16 @@ __global__ __launch_bounds__(1024) void decode_generic_kernel(const uint8_t* __r
                 else
                     *reinterpret_cast<f16x8*>(dst + p * 8) = o;
             }
-        } else {
+        } else if constexpr (G > 1) {
+            // one G-entry store per group: w is 16-byte aligned, so group gid starts at a
+            // multiple of 2 G bytes; non-temporal, as above
+            typedef _Float16 f16xg __attribute__((ext_vector_type(G)));
+            f16xg o;
 #pragma unroll
-            for (int t = 0; t < G; ++t) dst[t] = (f16)__fmul_rn(v[t], s);
+            for (int t = 0; t < G; ++t) o[t] = (f16)__fmul_rn(v[t], s);
+            __builtin_nontemporal_store(o, reinterpret_cast<f16xg*>(dst));
+        } else {
+            dst[0] = (f16)__fmul_rn(v[0], s);
         }
     }
 }
@@ -353,34 +380,43 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const uint8_t* __rest
 
 size_t codebook_bytes(const GenericScheme& sc) { return ((size_t)sc.M << sc.B) * (size_t)sc.g * 2; }
 
-template <int G, int CB>
-hipError_t decode_g(const GenericScheme& sc, const void* codes, const void* codebooks, const void* scales,
-                    void* w, int64_t out, int64_t in, hipStream_t stream) {
+template <int G, int CB, int KG>
+hipError_t decode_gk(const GenericScheme& sc, const void* codes, const void* codebooks, const void* scales,
+                     void* w, int64_t out, int64_t in, hipStream_t stream) {
     const uint32_t n_grp_row = (uint32_t)(in / G);
-    const uint64_t n_groups = (uint64_t)out * n_grp_row;
+    const uint64_t n_units = (uint64_t)out * n_grp_row / KG;
     const size_t lds = codebook_bytes(sc);
     if (lds <= kGemvLdsCodebook) {   // codebooks in LDS: one or two 1024-thread workgroups per CU
-        auto kern = decode_generic_kernel<G, CB, true>;
+        auto kern = decode_generic_kernel<G, CB, true, KG>;
         if (lds > 65536) {
             const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)lds);
             if (e != hipSuccess) return e;
         }
-        uint64_t blocks = (n_groups + 1023) / 1024;
+        uint64_t blocks = (n_units + 1023) / 1024;
         const uint64_t max_blocks = (uint64_t)device_cu_count() * (lds <= 65536 ? 2 : 1);
         if (blocks > max_blocks) blocks = max_blocks;
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(1024), lds, stream, (const uint8_t*)codes,
-                           (const f16*)codebooks, (const f16*)scales, (f16*)w, (uint32_t)n_groups, n_grp_row, sc.M,
+                           (const f16*)codebooks, (const f16*)scales, (f16*)w, (uint32_t)n_units, n_grp_row, sc.M,
                            sc.B);
         return hipGetLastError();
     }
-    uint64_t blocks = (n_groups + 255) / 256;
+    uint64_t blocks = (n_units + 255) / 256;
     const uint64_t max_blocks = (uint64_t)device_cu_count() * 16;
     if (blocks > max_blocks) blocks = max_blocks;
-    hipLaunchKernelGGL((decode_generic_kernel<G, CB, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((decode_generic_kernel<G, CB, false, KG>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales, (f16*)w,
-                       (uint32_t)n_groups, n_grp_row, sc.M, sc.B);
+                       (uint32_t)n_units, n_grp_row, sc.M, sc.B);
     return hipGetLastError();
+}
+
+template <int G, int CB>
+hipError_t decode_g(const GenericScheme& sc, const void* codes, const void* codebooks, const void* scales,
+                    void* w, int64_t out, int64_t in, hipStream_t stream) {
+    if constexpr (G < 8) {
+        if (in % 8 == 0) return decode_gk<G, CB, 8 / G>(sc, codes, codebooks, scales, w, out, in, stream);
+    }
+    return decode_gk<G, CB, 1>(sc, codes, codebooks, scales, w, out, in, stream);
 }
 
 template <int G, int CB, bool LDS>

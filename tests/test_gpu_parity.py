@@ -392,6 +392,18 @@ def test_generic_decode_bit_exact(M, B, g):
     np.testing.assert_array_equal(w.cpu().numpy().view(np.uint16), want.view(np.uint16))
 
 
+@pytest.mark.parametrize("M,B,g", [(1, 8, 4), (3, 5, 2), (1, 12, 1), (1, 16, 4), (1, 12, 4)])
+def test_generic_decode_bit_exact_whole_pieces(M, B, g):
+    """g < 8 with in % 8 == 0: a thread decodes 8/g groups of one row into one 16-byte store."""
+    L = synth.make_layer_mbg(M, B, g, 67, 8 * 41, seed=M + B + g + 1)
+    codes = junk_high_bits(L.codes, B)
+    c, cb, s, _ = gdev(L, codes)
+    w = E.aqlm_linear_decode(c, cb, s)
+    torch.cuda.synchronize()
+    want = O.decode_fp16(codes, L.codebooks, L.scales)
+    np.testing.assert_array_equal(w.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
 @pytest.mark.parametrize("M,B,g", GENERIC)
 @pytest.mark.parametrize("batch", [1, 5, 16])
 def test_generic_gemv(M, B, g, batch):
