@@ -16,7 +16,9 @@
  * all cost 2 bits per weight): 1 <= M <= AQLM_MAX_CODEBOOKS, 1 <= B <= 16,
  * g in {1, 2, 4, 8, 16, 32}.  The two named there as XBit-MxB at g = 8,
  * (1, 16, 8) "1x16" and (2, 8, 8) "2x8", run tuned kernels; every other
- * triple runs general kernels with the same semantics.
+ * triple runs general kernels with the same semantics, except that the GEMV
+ * of the other 2-bit triples with B = 8 ((1, 8, 4), (4, 8, 16), and
+ * (8, 8, 32) above batch 8) runs the tuned 2x8 kernel when in % 8 == 0.
  *
  * Memory layouts (all arrays contiguous, row-major, DEVICE pointers):
  *   codes      [out][in/g][M]  uint8 for B <= 8; 16-bit (int16) for
@@ -102,7 +104,9 @@ int aqlm_linear_gemv(const void* codes, const void* codebooks, const void* scale
  * with outs[l] == 0 is skipped.  1 <= n_layers <= AQLM_FUSED_MAX_LAYERS
  * (else AQLM_ERR_SHAPE); a NULL array gives AQLM_ERR_NULL.  The results are
  * bit-identical to n_layers separate aqlm_linear_gemv calls; fusing pays the
- * launch and the per-workgroup start-up latencies once for the group.
+ * launch and the per-workgroup start-up latencies once for the group.  (The
+ * triples whose GEMV runs a general kernel are served by one launch per
+ * layer.)
  */
 int aqlm_linear_gemv_fused(int n_layers, const void* const* codes, const void* const* codebooks,
                            const void* const* scales, const int64_t* outs, const void* x,
