@@ -154,6 +154,8 @@ int aqlm_linear_gemm(const void* codes, const void* codebooks, const void* scale
     bool empty = false;
     const int st = validate(Op::kGemm, codes, codebooks, scales, x, y, M, B, g, out, in, batch, &scheme, &empty);
     if (st != AQLM_OK || empty) return st;
+    if (M == 1 && B == 8 && g == 4 && in % 64 == 0)   // the 2x8 pipeline with two 4-entry codewords a piece
+        return finish(launch_gemm_pipe_1x8g4(codes, codebooks, scales, x, y, out, in, batch, (hipStream_t)stream));
     if (scheme == kSchemeGeneric)
         return finish(launch_gemm_generic(GenericScheme{M, B, g}, codes, codebooks, scales, x, y, out, in,
                                           batch, (hipStream_t)stream));

@@ -61,6 +61,10 @@ hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, con
 hipError_t launch_gemm_pipe_2x8(const void* codes, const void* codebooks, const void* scales,
                                 const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                                 hipStream_t stream);
+// The same pipeline for 1x8 g4 (its codes also take 2 bytes per 8 inputs); in % 64 == 0.
+hipError_t launch_gemm_pipe_1x8g4(const void* codes, const void* codebooks, const void* scales,
+                                  const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                                  hipStream_t stream);
 
 // Dense fp16 product y[t][i] = sum_k x[t][k] w16[i][k] (gemm_dense.hip); requires in % 64 == 0.
 hipError_t launch_gemm_dense(const void* x, const void* w16, void* y, int64_t out, int64_t in, int64_t batch,

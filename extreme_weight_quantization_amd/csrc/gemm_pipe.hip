@@ -1,5 +1,8 @@
 // Prefill product for the 2x8 scheme with a role-split software pipeline:
 //   Y[t][i] = s[i] * sum_k X[t][k] Wc[i][k],  Wc[i][8j+u] = C0[b0][u] + C1[b1][u].
+// The same kernel serves 1x8 g4, whose codes also take 2 bytes per 8 inputs at
+// the same places: there the 8 weights of a piece are two 4-entry codewords,
+// Wc[i][8j+u] = C0[b_{2j}][u] for u < 4 and C0[b_{2j+1}][u-4] above.
 //
 // "The AQLM Quantization Algorithm, Explained", Figure 2 of the MCQ section:
 // the product runs on dequantized half-precision weights, each built from one
@@ -33,7 +36,7 @@
 //                     B_k waits for the codes of step k+2.
 // X tiles thus have two steps to arrive, code loads about kRing-2.  X keeps
 // three stages, W two (a W tile is written one step before it is read), the
-// code ring kRing steps: 96 + 32 + 24 + 8 (codebooks) = 160 KB.  The products
+// code ring kRing steps: 96 + 32 + 24 + 8 (codebooks; 2 KB for 1x8 g4) = 160 KB.  The products
 // run in the order of a plain k loop.
 //
 // Epilogue (out % 8 == 0): producers and consumers meet at a last barrier; then
@@ -63,7 +66,10 @@ constexpr int kPipeXStage = kPipeBM * 8;     // 16-byte slots of one X stage (a 
 constexpr int kPipeWStage = kPipeBN * 8;     // 16-byte slots of one W stage
 constexpr int kPipeWStages = 2;
 constexpr int kPipeRing = 12;                // steps of codes held in LDS
-constexpr int kPipeCb = 2 * kCodewords2x8;   // codebook slots: codeword k of codebook m at 2k+m
+// codebook slots: 2x8 codeword k of codebook m at 2k+m; 1x8 g4 codeword k in 8-byte slot k
+template <int SCHEME>
+constexpr int pipe_cb_slots() { return SCHEME == kScheme2x8 ? 2 * kCodewords2x8 : kCodewords2x8 / 2; }
+constexpr int kPipeCb = pipe_cb_slots<kScheme2x8>();   // the larger of the two
 constexpr int kPipeXOff = 0;
 constexpr int kPipeWOff = kPipeXOff + 3 * kPipeXStage;
 constexpr int kPipeRingOff = kPipeWOff + kPipeWStages * kPipeWStage;
@@ -73,6 +79,7 @@ static_assert(kPipeLds <= 163840, "LDS budget");
 
 __device__ __forceinline__ int stage_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
 
+template <int SCHEME>
 __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
     const uint8_t* __restrict__ codes, const f16* __restrict__ codebooks,
     const f16* __restrict__ scales, const f16* __restrict__ x, f16* __restrict__ y,
@@ -89,8 +96,14 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
     const int n0 = (int)(blockIdx.x / n_tt) * kPipeBN;
     const int t0 = (int)(blockIdx.x % n_tt) * kPipeBM;
 
-    for (int j = tid; j < kPipeCb; j += kPipeThreads)
-        cb[j] = load16(codebooks + (size_t)((j & 1) * kCodewords2x8 + (j >> 1)) * kGroup);
+    if constexpr (SCHEME == kScheme2x8) {
+        for (int j = tid; j < kPipeCb; j += kPipeThreads)
+            cb[j] = load16(codebooks + (size_t)((j & 1) * kCodewords2x8 + (j >> 1)) * kGroup);
+    } else {
+        u32x2* cb8 = reinterpret_cast<u32x2*>(cb);
+        for (int j = tid; j < kCodewords2x8; j += kPipeThreads)
+            cb8[j] = *reinterpret_cast<const u32x2*>(codebooks + (size_t)j * 4);
+    }
 
     if (wave >= kPipeConsumers) {
         // ------------------------------ producers ------------------------------
@@ -115,17 +128,33 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
         auto decode_step = [&](int j) {
             const uint32_t* cr = reinterpret_cast<const uint32_t*>(ring + (j % kPipeRing) * kPipeBN + r);
             const uint32_t ca = cr[c0 >> 1], cw = cr[(c0 >> 1) + 1];
-            f16x8 e[8];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                e[2 * q] = as_f16x8(cb[2 * ((ca >> (16 * q)) & 0xff)]);
-                e[2 * q + 1] = as_f16x8(cb[2 * ((ca >> (16 * q + 8)) & 0xff) + 1]);
-                e[4 + 2 * q] = as_f16x8(cb[2 * ((cw >> (16 * q)) & 0xff)]);
-                e[5 + 2 * q] = as_f16x8(cb[2 * ((cw >> (16 * q + 8)) & 0xff) + 1]);
-            }
             u32x4* d = Ws + (j % kPipeWStages) * kPipeWStage;
+            if constexpr (SCHEME == kScheme2x8) {
+                f16x8 e[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) d[stage_slot(r, c0 + q)] = as_u32x4(e[2 * q] + e[2 * q + 1]);
+                for (int q = 0; q < 2; ++q) {
+                    e[2 * q] = as_f16x8(cb[2 * ((ca >> (16 * q)) & 0xff)]);
+                    e[2 * q + 1] = as_f16x8(cb[2 * ((ca >> (16 * q + 8)) & 0xff) + 1]);
+                    e[4 + 2 * q] = as_f16x8(cb[2 * ((cw >> (16 * q)) & 0xff)]);
+                    e[5 + 2 * q] = as_f16x8(cb[2 * ((cw >> (16 * q + 8)) & 0xff) + 1]);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) d[stage_slot(r, c0 + q)] = as_u32x4(e[2 * q] + e[2 * q + 1]);
+            } else {
+                // piece c0 + q: groups 2 (c0 + q) and 2 (c0 + q) + 1, one byte each
+                const u32x2* cb8 = reinterpret_cast<const u32x2*>(cb);
+                u32x2 e[8];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    e[2 * q] = cb8[(ca >> (16 * q)) & 0xff];
+                    e[2 * q + 1] = cb8[(ca >> (16 * q + 8)) & 0xff];
+                    e[4 + 2 * q] = cb8[(cw >> (16 * q)) & 0xff];
+                    e[5 + 2 * q] = cb8[(cw >> (16 * q + 8)) & 0xff];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    d[stage_slot(r, c0 + q)] = u32x4{e[2 * q][0], e[2 * q][1], e[2 * q + 1][0], e[2 * q + 1][1]};
+            }
         };
 #pragma unroll
         for (int j = 0; j < kPipeRing; ++j) load_codes(j);
@@ -274,18 +303,31 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
 
 }  // namespace
 
-hipError_t launch_gemm_pipe_2x8(const void* codes, const void* codebooks, const void* scales,
-                                const void* x, void* y, int64_t out, int64_t in, int64_t batch,
-                                hipStream_t stream) {
+template <int SCHEME>
+static hipError_t launch_pipe(const void* codes, const void* codebooks, const void* scales, const void* x, void* y,
+                              int64_t out, int64_t in, int64_t batch, hipStream_t stream) {
     if (in % 64 != 0) return hipErrorInvalidValue;
-    const hipError_t e = hipFuncSetAttribute((const void*)gemm_pipe_2x8_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPipeLds);
+    const size_t lds = kPipeLds - (size_t)(kPipeCb - pipe_cb_slots<SCHEME>()) * 16;
+    const hipError_t e = hipFuncSetAttribute((const void*)gemm_pipe_2x8_kernel<SCHEME>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(((out + kPipeBN - 1) / kPipeBN) * ((batch + kPipeBM - 1) / kPipeBM)));
-    hipLaunchKernelGGL(gemm_pipe_2x8_kernel, grid, dim3(kPipeThreads), kPipeLds, stream,
+    hipLaunchKernelGGL(gemm_pipe_2x8_kernel<SCHEME>, grid, dim3(kPipeThreads), lds, stream,
                        (const uint8_t*)codes, (const f16*)codebooks, (const f16*)scales, (const f16*)x,
                        (f16*)y, (int)out, (int)in, (int)batch);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_pipe_2x8(const void* codes, const void* codebooks, const void* scales,
+                                const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                                hipStream_t stream) {
+    return launch_pipe<kScheme2x8>(codes, codebooks, scales, x, y, out, in, batch, stream);
+}
+
+hipError_t launch_gemm_pipe_1x8g4(const void* codes, const void* codebooks, const void* scales,
+                                  const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                                  hipStream_t stream) {
+    return launch_pipe<kSchemeB8M1>(codes, codebooks, scales, x, y, out, in, batch, stream);
 }
 
 }  // namespace aqlm

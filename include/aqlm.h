@@ -18,7 +18,8 @@
  * (1, 16, 8) "1x16" and (2, 8, 8) "2x8", run tuned kernels; every other
  * triple runs general kernels with the same semantics, except that the GEMV
  * of the other 2-bit triples with B = 8 ((1, 8, 4), (4, 8, 16), and
- * (8, 8, 32) above batch 8) runs the tuned 2x8 kernel when in % 8 == 0.
+ * (8, 8, 32) above batch 8) runs the tuned 2x8 kernel when in % 8 == 0, and
+ * the prefill GEMM of (1, 8, 4) the tuned 2x8 pipeline when in % 64 == 0.
  *
  * Memory layouts (all arrays contiguous, row-major, DEVICE pointers):
  *   codes      [out][in/g][M]  uint8 for B <= 8; 16-bit (int16) for

@@ -492,6 +492,18 @@ def test_generic_gemm(M, B, g, out, n_grp, batch):
                  f"gemm {M}x{B}g{g} {out}x{g * n_grp} T{batch}")
 
 
+@pytest.mark.parametrize("out,n_in,batch", [(300, 1088, 130), (129, 64, 257), (64, 2048, 1)])
+def test_gemm_1x8g4_pipeline(out, n_in, batch):
+    """1x8 g4 with in % 64 == 0 runs the pipelined 2x8 prefill: ragged rows and tokens, a
+    single k-step, a single token."""
+    L = synth.make_layer_mbg(1, 8, 4, out, n_in, batch=batch, seed=out + batch)
+    c, cb, s, x = gdev(L, L.codes)
+    y = E.aqlm_linear_gemm(c, cb, s, x)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy().astype(np.float64), O.linear_ref_f64(L.codes, L.codebooks, L.scales, L.x),
+                 f"1x8g4 gemm {out}x{n_in} T{batch}")
+
+
 @pytest.mark.parametrize("M,B,g", [(4, 8, 16), (1, 8, 4), (3, 5, 2)])
 def test_generic_exact_on_identity(M, B, g):
     """Dyadic one-hot codebooks and X = I: GEMM and GEMV return W16 columns exactly."""
