@@ -32,6 +32,10 @@
 //    LDS outweighs the extra conflicts) up to batch 8; with the 16-row x
 //    stage (128 KB) above batch 8 only 4 replicas fit.  1x16 codewords are
 //    gathered from the L2-resident 1 MiB codebook;
+//  * the other 2-bit schemes with B = 8 ("Key AQLM quantization parameters":
+//    1x8 g4, 4x8 g16, 8x8 g32 cost the same bits as 2x8) store in/4 code bytes
+//    per row too, so the same decomposition serves them; only the decode of a
+//    piece of 8 inputs and the codebook copy differ (chunk_mfma, cb_slots);
 //  * per-wave partial tiles are summed in LDS; the row scale is applied once
 //    in fp32 and y is rounded to fp16.
 //
