@@ -523,9 +523,11 @@ static hipError_t launch_gemv_2x8(const GemvLayers& layers, const void* x, int n
 }
 
 // The other 2-bit B = 8 schemes: as 2x8, with the replicas that fit next to the x stage.
-// 1x8 g4 (2 KB a copy): 8 replicas.  4x8 g16 (32 KB): 2, and 1 with the 16-row stage.
-// 8x8 g32 (128 KB): one copy and direct x loads (no room for a stage); its launcher
-// takes it only above batch 8.
+// 1x8 g4 (2 KB a copy): 8 replicas.  4x8 g16 (32 KB a copy, four lookups a piece, bound
+// by LDS bank conflicts): direct x with 4 replicas at batches 1-2 and above 8, the 8-row
+// stage with 3 replicas at 3-8 (measured faster than the 16-row stage, which leaves room
+// for one copy, on the 11008-row and 11008-input layers).  8x8 g32 (128 KB): one copy
+// and direct x loads (no room for a stage); its launcher takes it only above batch 8.
 template <int RTP>
 static hipError_t launch_gemv_b8(int scheme, const GemvLayers& layers, const void* x, int n, int T,
                                  hipStream_t stream) {
@@ -535,9 +537,9 @@ static hipError_t launch_gemv_b8(int scheme, const GemvLayers& layers, const voi
         return launch_gemv_v<kSchemeB8M1, 8, RTP, kXStaged16>(layers, x, n, T, stream);
     }
     if (scheme == kSchemeB8M4) {
-        if (T <= kGemvDirectBatch2x8) return launch_gemv_v<kSchemeB8M4, 2, RTP, kXDirect>(layers, x, n, T, stream);
-        if (T <= kGemvStage8Batch) return launch_gemv_v<kSchemeB8M4, 2, RTP, kXStaged8>(layers, x, n, T, stream);
-        return launch_gemv_v<kSchemeB8M4, 1, RTP, kXStaged16>(layers, x, n, T, stream);
+        if (T > kGemvDirectBatch2x8 && T <= kGemvStage8Batch)
+            return launch_gemv_v<kSchemeB8M4, 3, RTP, kXStaged8>(layers, x, n, T, stream);
+        return launch_gemv_v<kSchemeB8M4, 4, RTP, kXDirect>(layers, x, n, T, stream);
     }
     return launch_gemv_v<kSchemeB8M8, 1, RTP, kXDirect>(layers, x, n, T, stream);
 }
