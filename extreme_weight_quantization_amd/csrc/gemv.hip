@@ -57,7 +57,13 @@ constexpr int kGemvWaves = 16;
 constexpr int kGemvThreads = kGemvWaves * kWave;
 constexpr int kSlabGroups = 32;          // groups per slab (8 products x 4 k-quarters)
 constexpr int kRowTile = 16;
-constexpr int kRedFloats = kRowTile * 16; // one 16x16 fp32 tile per wave
+constexpr int kRedFloats = kRowTile * 16; // one 16x16 fp32 tile per wave (outputs of a row tile)
+// A wave's tile in LDS: row r (output row), column b (batch) at r * 17 + b.  The odd
+// stride puts the four k-quarters' writes of one column, and the 16 rows that the
+// summing threads read for one column, in distinct bank groups (a stride of 16 made
+// both 4-way conflicts).
+constexpr int kRedRow = 17;
+constexpr int kRedStride = kRowTile * kRedRow;
 
 // How a wave gets the activation operand of a slab (x of 16 batch columns x 32
 // groups) into registers:
@@ -394,7 +400,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
             if (rt >= n_rt) break;
             __syncthreads();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave * kRedFloats + (4 * kq + r) * 16 + lrow] = acc[i][r];
+            for (int r = 0; r < 4; ++r) red[wave * kRedStride + (4 * kq + r) * kRedRow + lrow] = acc[i][r];
             __syncthreads();
             if (tid < kRedFloats) {
                 const int b = tid / kRowTile, rr = tid % kRowTile;
@@ -402,7 +408,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
                 if (b < T && row < out) {
                     float sum = 0.f;
 #pragma unroll
-                    for (int w = 0; w < kGemvWaves; ++w) sum += red[w * kRedFloats + rr * 16 + b];
+                    for (int w = 0; w < kGemvWaves; ++w) sum += red[w * kRedStride + rr * kRedRow + b];
                     y[(size_t)b * out + row] = (f16)(sum * (float)scales[row]);
                 }
             }
@@ -452,7 +458,7 @@ static hipError_t launch_gemv_t(const GemvLayers& layers, const void* x, int in,
     const void* kern = fused ? (const void*)gemv_fused_kernel<SCHEME, REPL, VEC, RTP, XM>
                              : (const void*)gemv_kernel<SCHEME, REPL, VEC, RTP, XM>;
     const size_t lds = (size_t)cb_slots<SCHEME, REPL>() * 16 +
-                       std::max((size_t)kGemvWaves * kRedFloats * sizeof(float),
+                       std::max((size_t)kGemvWaves * kRedStride * sizeof(float),
                                 (size_t)kGemvWaves * kXStageSlots(XM) * 16);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
