@@ -599,6 +599,39 @@ def test_kmeans_init_bit_exact(M, B, g, out, n_in, iters):
     np.testing.assert_array_equal(codes.cpu().numpy(), codes_ref)
 
 
+@pytest.mark.parametrize("B,g", [(11, 8), (12, 4)])
+def test_encode_greedy_ties_across_chunks(B, g):
+    """Codebooks made of repeated 1024-codeword blocks: equal distances in different 1024-codeword
+    chunks go to the lowest index, as in the oracle (codes all below 1024, bit-identical)."""
+    rng = np.random.default_rng(B)
+    base = rng.normal(0, 1, size=(1024, g)).astype(np.float16)
+    cb = np.concatenate([base] * ((1 << B) // 1024))[None]
+    w, s = weights(40, 24 * g, seed=B)
+    codes = E.aqlm_encode_greedy(torch.from_numpy(w).cuda(), torch.from_numpy(s).cuda(), torch.from_numpy(cb).cuda())
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    np.testing.assert_array_equal(got, O.encode_greedy(w, s, cb))
+    assert int(got.view(np.uint16).max()) < 1024
+
+
+def test_kmeans_init_bit_exact_members_near_the_fixed_point_grid():
+    """Weights that are small multiples of 2^-24 (fp16 subnormals) over scales 0.5 .. 4: the targets
+    fall on and between multiples of 2^-24, halves included, so the centroid sums exercise the
+    rounding to the fixed-point grid (halves to even); codebooks and codes equal the oracle's."""
+    rng = np.random.default_rng(21)
+    out, n_in, g, B, M = 48, 64, 4, 6, 2
+    w = (rng.integers(-6, 7, size=(out, n_in)) * 2.0 ** -24).astype(np.float16)
+    s = rng.choice([0.5, 0.75, 1.5, 3.0, 4.0], size=out).astype(np.float16)
+    N = out * n_in // g
+    seeds = np.stack([rng.choice(N, 1 << B, replace=False) for _ in range(M)]).astype(np.int64)
+    cb, codes = E.aqlm_kmeans_init(torch.from_numpy(w).cuda(), torch.from_numpy(s).cuda(),
+                                   torch.from_numpy(seeds).cuda(), B, g, 3)
+    torch.cuda.synchronize()
+    cb_ref, codes_ref = O.kmeans_residual_init(w, s, seeds, M, B, g, 3)
+    np.testing.assert_array_equal(cb.cpu().numpy().view(np.uint16), cb_ref.view(np.uint16))
+    np.testing.assert_array_equal(codes.cpu().numpy(), codes_ref)
+
+
 def test_encode_and_kmeans_full_size_2x8():
     """4096x4096 weights: encoder codes on sampled rows equal the oracle's; the k-means codes are the
     greedy encoding against the k-means codebooks (checked on sampled rows)."""

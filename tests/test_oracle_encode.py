@@ -181,3 +181,105 @@ def test_residual_kmeans_on_planted_clusters_recovers_the_layer():
     cb, codes = O.kmeans_residual_init(w, s, seeds, 1, B, g, iters=2)
     np.testing.assert_array_equal(O.decode_fp16(codes, cb, s), w)
     assert codes.max() < K   # duplicates of seed 0 tie with it and lose
+
+
+def test_greedy_ties_across_candidate_chunks_take_the_lowest_index():
+    """B = 11: codeword k + 1024 repeats codeword k, so the two sit in different 1024-codeword
+    chunks of the scan.  The lowest index must still win: every code is below 1024 and equals
+    the float64 nearest codeword among the first 1024 (the pages' tie rule is silent; the
+    reading is the lowest index, the same as within one chunk)."""
+    rng = np.random.default_rng(11)
+    base = rng.normal(0, 1, size=(1024, 8)).astype(np.float16)
+    cb = np.concatenate([base, base])[None]              # [1][2048][8]
+    w = rng.normal(0, 1, size=(16, 64)).astype(np.float16)
+    codes = O.encode_greedy(w, np.ones(16, np.float16), cb)
+    idx = codes.view(np.uint16).astype(np.int64).reshape(-1)
+    assert idx.max() < 1024
+    r = w.astype(np.float64).reshape(-1, 8)
+    dist = ((r[:, None, :] - base.astype(np.float64)[None]) ** 2).sum(-1)
+    np.testing.assert_array_equal(idx, np.argmin(dist, axis=1))
+
+
+def test_greedy_tie_rule_holds_in_every_chunk():
+    """B = 12 with four copies of a 1024-codeword block: codes stay in the first block, so a later
+    chunk never replaces an equal distance found in an earlier one, whichever chunk it is."""
+    rng = np.random.default_rng(12)
+    base = rng.normal(0, 1, size=(1024, 4)).astype(np.float16)
+    cb = np.concatenate([base] * 4)[None]
+    w = rng.normal(0, 1, size=(8, 64)).astype(np.float16)
+    codes = O.encode_greedy(w, np.ones(8, np.float16), cb)
+    assert int(codes.view(np.uint16).max()) < 1024
+
+
+# Centroids under the fixed-point reading.  The expected values below were worked by hand
+# from the reading's statement (each coordinate rounded to the nearest multiple of 2^-24,
+# halves to even, the multiples summed exactly, the sum divided by the member count and
+# rounded to fp32); they are not recomputed with the oracle's own formula.
+U24 = 2.0 ** -24
+
+
+def _one_cluster_centroid(members):
+    r = np.array(members, np.float32)[:, None]
+    return float(O.kmeans_centroids(r, np.zeros(len(members), np.int64), np.zeros((1, 1), np.float32))[0, 0])
+
+
+def test_kmeans_centroid_fixed_point_worked_by_hand():
+    # 0.75, 1.25 and 16.5 units of 2^-24 round to 1, 1 and 16 (16.5: the even neighbour):
+    # sum 18, mean exactly 6 units (the exact mean would be 6.1666... units).
+    assert _one_cluster_centroid([3 * 2.0 ** -26, 5 * 2.0 ** -26, 66 * 2.0 ** -26]) == 6 * U24
+    # halves go to the even neighbour: 2.5 -> 2, 3.5 -> 4, -2.5 -> -2, -0.5 -> 0: sum 4, mean 1 unit
+    # (the exact mean is 0.75 units; floor would give 0.25, halves away from zero 0.75).
+    assert _one_cluster_centroid([2.5 * U24, 3.5 * U24, -2.5 * U24, -0.5 * U24]) == U24
+    # members far below one unit vanish: the centroid of two 1e-9 members is exactly 0.
+    assert _one_cluster_centroid([1e-9, 1e-9]) == 0.0
+    # 1000 and 2^-26 (0.25 units -> 0): 1000 * 2^24 / 2 = 500 exactly.
+    assert _one_cluster_centroid([1000.0, 2.0 ** -26]) == 500.0
+    # three members 1, 1, 2 units: 4/3 units, rounded once to fp32 (not a multiple of 2^-24).
+    assert _one_cluster_centroid([U24, U24, 2 * U24]) == float(np.float32(4.0 / 3.0 * U24))
+
+
+def test_kmeans_centroid_against_the_exactly_rounded_mean():
+    """Adversarial clusters (members below 2^-24, mixed magnitudes, near-cancelling signs): the
+    fixed-point centroid is within 2^-25 + half an fp32 ulp of the exact rational mean, and its
+    fp16 rounding (the codebook entry) equals the fp16 rounding of the exact mean except where
+    an fp16 rounding midpoint lies within that distance of the exact mean.  Such boundary cases
+    are counted: the planted ones (members of 0.49, 0.49 and 0.6 units of 2^-24, fixed-point
+    mean 1/3 unit, exact mean 0.527 unit, on either side of the 0.5-unit midpoint) always are,
+    plain random clusters never are."""
+    from fractions import Fraction
+    rng = np.random.default_rng(13)
+    K, per = 96, 7
+    kinds = []
+    pts = []
+    for k in range(K):
+        kind = k % 5
+        if kind == 0:     # tiny members only
+            v = rng.normal(0, 2.0 ** -25, size=per)
+        elif kind == 1:   # one large member among tiny ones
+            v = np.concatenate([[rng.normal(0, 50)], rng.normal(0, 2.0 ** -26, size=per - 1)])
+        elif kind == 2:   # near-cancelling pairs
+            a = rng.normal(0, 3, size=per // 2)
+            v = np.concatenate([a, -a + rng.normal(0, 2.0 ** -22, size=a.size), [rng.normal(0, 1e-3)]])
+        elif kind == 3:   # plain random cluster
+            v = rng.normal(0, 1, size=per)
+        else:             # planted: straddles the fp16 midpoint at half the smallest subnormal
+            v = np.array([0.49, 0.49, 0.6] * 2 + [0.49]) * U24
+        pts.append(v.astype(np.float32))
+        kinds.append(kind)
+    r = np.concatenate(pts)[:, None]
+    labels = np.repeat(np.arange(K), per)
+    c = O.kmeans_centroids(r, labels, np.zeros((K, 1), np.float32))[:, 0]
+    boundary = []
+    for k in range(K):
+        exact = sum(Fraction(float(v)) for v in pts[k]) / per
+        half_ulp = Fraction(float(np.spacing(np.float32(abs(float(exact)) or 1e-45)))) / 2
+        bound = Fraction(1, 2 ** 25) + half_ulp
+        assert abs(Fraction(float(c[k])) - exact) <= bound, (k, kinds[k])
+        e16, c16 = np.float16(np.float32(float(exact))), np.float16(c[k])
+        if c16 != e16:
+            boundary.append(kinds[k])
+            a = min(e16, c16)
+            mid = (Fraction(float(a)) + Fraction(float(np.nextafter(a, np.float16(np.inf))))) / 2
+            assert abs(mid - exact) <= bound
+    print(f"fp16 codebook entries that differ from the exactly rounded mean: {len(boundary)} of {K}")
+    assert boundary.count(4) == K // 5 and 3 not in boundary

@@ -50,6 +50,12 @@ ENCODE_MUTANTS = {
         " / KMEANS_FIXED_POINT / counts[nz, None].astype(np.float64)).astype(np.float32)",
         " / KMEANS_FIXED_POINT).astype(np.float32)"),
     "kmeans_residual_not_chained": ("        r = r - cb[idx[:, m]]\n    return codebooks", "    return codebooks"),
+    "chunk_ties_take_later": ("upd = dd < best_d", "upd = dd <= best_d"),
+    "centroid_plain_float_mean": (
+        "q = np.rint(r.astype(np.float64) * KMEANS_FIXED_POINT).astype(np.int64)\n    sums = np.zeros((K, g), np.int64)",
+        "q = r.astype(np.float64) * KMEANS_FIXED_POINT\n    sums = np.zeros((K, g), np.float64)"),
+    "centroid_rounds_down": ("q = np.rint(r.astype", "q = np.floor(r.astype"),
+    "centroid_finer_grid": ("KMEANS_FIXED_POINT = 2.0 ** 24", "KMEANS_FIXED_POINT = 2.0 ** 30"),
     "targets_times_scale": ("r = w.astype(np.float32) / scales.astype(np.float32)[:, None]",
                             "r = w.astype(np.float32) * scales.astype(np.float32)[:, None]"),
 }
