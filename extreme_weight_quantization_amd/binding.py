@@ -124,14 +124,27 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _same_device(named):
+    """All tensors (name, tensor) on one GPU: the kernels get raw pointers of one device."""
+    devs = {(t.device.type, t.device.index) for _, t in named if t is not None}
+    if len(devs) > 1:
+        raise ValueError("tensors are on different devices: " +
+                         ", ".join(f"{n} on {t.device}" for n, t in named if t is not None))
+
+
 def _check_tensors(codes, codebooks, scales, x):
-    for name, t in (("codes", codes), ("codebooks", codebooks), ("scales", scales), ("x", x)):
+    """Device, dtype, contiguity and the shapes that tie codes, codebooks and scales together
+    (codes [out][in/g][M] with M from the codebooks, scales [out]); a mismatch would make the
+    kernels read past a buffer, so it is refused here, before any launch."""
+    named = (("codes", codes), ("codebooks", codebooks), ("scales", scales), ("x", x))
+    for name, t in named:
         if t is None:
             continue
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    _same_device(named)
     if codebooks.dtype != torch.float16 or scales.dtype != torch.float16:
         raise ValueError("codebooks and scales must be float16")
     if codes.dtype not in (torch.uint8, torch.int16):
@@ -140,6 +153,11 @@ def _check_tensors(codes, codebooks, scales, x):
         raise ValueError("x must be float16")
     if codes.dim() != 3:
         raise ValueError("codes must be [out][in/g][M]")
+    if codebooks.dim() == 3 and codes.shape[2] != codebooks.shape[0]:
+        raise ValueError(f"codes hold {codes.shape[2]} codes per group but there are "
+                         f"{codebooks.shape[0]} codebooks")
+    if scales.shape != (codes.shape[0],):
+        raise ValueError(f"scales must be [{codes.shape[0]}] (one per output row)")
 
 
 def _linear(fn_name, codes, codebooks, scales, x, y):
@@ -154,6 +172,7 @@ def _linear(fn_name, codes, codebooks, scales, x, y):
         y = torch.empty((batch, out), dtype=torch.float16, device=x.device)
     elif y.shape != (batch, out) or y.dtype != torch.float16 or not y.is_contiguous():
         raise ValueError(f"y must be a contiguous float16 [{batch}][{out}] tensor")
+    _same_device((("x", x), ("y", y)))
     fn = getattr(load_library(), fn_name)
     _check(fn(_ptr(codes), _ptr(codebooks), _ptr(scales), _ptr(x), _ptr(y), M, B, g,
               out, n_in, batch, _stream(x.device)))
@@ -199,6 +218,7 @@ def aqlm_linear_gemv_fused(layers, x, ys=None):
         for y, o in zip(ys, outs):
             if y.shape != (batch, o) or y.dtype != torch.float16 or not y.is_contiguous():
                 raise ValueError(f"y must be a contiguous float16 [{batch}][{o}] tensor")
+            _same_device((("x", x), ("y", y)))
     n = len(layers)
     arr = ctypes.c_void_p * n
     c_codes = arr(*[l[0].data_ptr() for l in layers])
@@ -241,6 +261,7 @@ def aqlm_linear_gemm_dequant(codes, codebooks, scales, x, y=None, workspace=None
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
     elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    _same_device((("x", x), ("y", y), ("workspace", workspace)))
     _check(load_library().aqlm_linear_gemm_dequant(_ptr(codes), _ptr(codebooks), _ptr(scales), _ptr(x), _ptr(y),
                                                    _ptr(workspace), workspace.numel(), M, B, g, out, n_in, batch,
                                                    _stream(x.device)))
@@ -256,6 +277,7 @@ def aqlm_linear_decode(codes, codebooks, scales, w=None):
         w = torch.empty((out, G * g), dtype=torch.float16, device=codes.device)
     elif w.shape != (out, G * g) or w.dtype != torch.float16 or not w.is_contiguous():
         raise ValueError(f"w must be a contiguous float16 [{out}][{G * g}] tensor")
+    _same_device((("codes", codes), ("w", w)))
     _check(load_library().aqlm_linear_decode(_ptr(codes), _ptr(codebooks), _ptr(scales), None,
                                              _ptr(w), M, B, g, out, G * g, 0, _stream(codes.device)))
     return w
@@ -291,6 +313,7 @@ def aqlm_encode_greedy(w, scales, codebooks, codes=None):
     _check_weights(w, scales, g)
     out, n_in = int(w.shape[0]), int(w.shape[1])
     codes = _codes_out(codes, out, n_in // g, M, B, w.device)
+    _same_device((("w", w), ("scales", scales), ("codebooks", codebooks), ("codes", codes)))
     _check(load_library().aqlm_encode_greedy(_ptr(w), _ptr(scales), _ptr(codebooks.contiguous()), _ptr(codes),
                                              M, B, g, out, n_in, _stream(w.device)))
     return codes
@@ -321,6 +344,8 @@ def aqlm_kmeans_init(w, scales, seeds, B, g, iters, codebooks=None, codes=None, 
     need = kmeans_workspace_bytes(M, B, g)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
+    _same_device((("w", w), ("scales", scales), ("seeds", seeds), ("codebooks", codebooks), ("codes", codes),
+                  ("workspace", workspace)))
     _check(load_library().aqlm_kmeans_init(_ptr(w), _ptr(scales), _ptr(seeds), _ptr(codebooks), _ptr(codes),
                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                                            M, B, g, out, n_in, int(iters), _stream(w.device)))
@@ -388,6 +413,8 @@ def aqlm_linear_gemv_lists(lists: SliceLists, codebooks, scales, x, y=None, work
         raise ValueError("codebooks must be [1][65536][8]")
     if x.dim() != 2 or x.shape[1] != lists.n_in or x.shape[0] > 1:
         raise ValueError(f"x must be [1][{lists.n_in}]")
+    if scales.shape != (lists.out,):
+        raise ValueError(f"scales must be [{lists.out}] (one per output row)")
     batch = int(x.shape[0])
     if y is None:
         y = torch.empty((batch, lists.out), dtype=torch.float16, device=x.device)
@@ -395,6 +422,8 @@ def aqlm_linear_gemv_lists(lists: SliceLists, codebooks, scales, x, y=None, work
         raise ValueError(f"y must be a contiguous float16 [{batch}][{lists.out}] tensor")
     if workspace is None:
         workspace = torch.empty(lists_workspace_bytes(lists.out, lists.n_in), dtype=torch.uint8, device=x.device)
+    _same_device((("table", lists.table), ("entries", lists.entries), ("codebooks", codebooks), ("scales", scales),
+                  ("x", x), ("y", y), ("workspace", workspace)))
     _check(load_library().aqlm_linear_gemv_lists(
         _ptr(lists.table), _ptr(lists.entries), lists.entries.numel(), _ptr(codebooks), _ptr(scales), _ptr(x),
         _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(), 1, 16, 8, lists.out, lists.n_in,
@@ -424,6 +453,12 @@ def aqlm_linear_gemv_lists_fused(layers, x, ys=None, workspace=None):
         for name, t in (("codebooks", cb), ("scales", s)):
             if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float16:
                 raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
+        if cb.shape != (1, 1 << 16, 8):
+            raise ValueError("codebooks must be [1][65536][8]")
+        if s.shape != (lists.out,):
+            raise ValueError(f"scales must be [{lists.out}] (one per output row)")
+        _same_device((("x", x), ("table", lists.table), ("entries", lists.entries), ("codebooks", cb),
+                      ("scales", s)))
     outs = [lists.out for lists, _, _ in layers]
     if ys is None:
         ys = [torch.empty((batch, o), dtype=torch.float16, device=x.device) for o in outs]

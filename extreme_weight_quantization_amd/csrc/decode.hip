@@ -30,8 +30,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint8_t* __restrict__
             cb_lds[i] = load16(codebooks + (size_t)i * kGroup);
         __syncthreads();
     }
-    const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x; gid < n_groups; gid += stride) {
+    // 64-bit loop index: n_groups may come within a stride of 2^32, where a 32-bit
+    // index would wrap and never leave the loop
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t gid64 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; gid64 < n_groups; gid64 += stride) {
+        const uint32_t gid = (uint32_t)gid64;
         const uint32_t row = gid / G;
         const float s = (float)scales[row];
         const uint32_t code = reinterpret_cast<const uint16_t*>(codes)[gid];

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kEncThreads) void assign_kernel(
     const f16* __restrict__ w, const f16* __restrict__ scales, const f16* __restrict__ codebooks,
     uint8_t* __restrict__ codes, const float* __restrict__ centroids, unsigned long long* __restrict__ sums,
     unsigned long long* __restrict__ counts, int64_t n_groups, int64_t groups_per_row, int in, int M, int B,
-    int m) {
+    int m, float lim = 0.f, unsigned long long* __restrict__ overflow = nullptr) {
     constexpr int kTile = kTileBytes / (4 * G);   // candidates per LDS tile
     __shared__ float tile[kTile * G];
     extern __shared__ unsigned long long lacc[];   // LACC: [K][G] sums, then [K] counts
@@ -137,9 +137,15 @@ __global__ __launch_bounds__(kEncThreads) void assign_kernel(
             if constexpr (KMEANS) {
                 unsigned long long* ps = LACC ? lacc : sums;
                 unsigned long long* pc = LACC ? lacc + (size_t)K * G : counts;
+                // a target at or above lim (or not finite) could carry a cluster's sum out of
+                // the exactly summed range: flag it, and the centroids come out NaN
+                bool bad = false;
+#pragma unroll
+                for (int t = 0; t < G; ++t) bad |= !(__builtin_fabsf(r[t]) < lim);
+                if (bad) atomicOr(overflow, 1ull);
 #pragma unroll
                 for (int t = 0; t < G; ++t) {
-                    const long long q = __double2ll_rn((double)r[t] * kFixedPoint);
+                    const long long q = bad ? 0ll : __double2ll_rn((double)r[t] * kFixedPoint);
                     atomicAdd(&ps[(size_t)best_k * G + t], (unsigned long long)q);
                 }
                 atomicAdd(&pc[best_k], 1ull);
@@ -182,10 +188,17 @@ __global__ __launch_bounds__(kEncThreads) void zero_kernel(unsigned long long* _
 }
 
 // Lloyd update: a non-empty cluster's centroid is its fixed-point sum / count (float64, then fp32).
+// A flagged overflow makes every centroid NaN (and so every later codebook).
 __global__ __launch_bounds__(kEncThreads) void update_kernel(const unsigned long long* __restrict__ sums,
                                                             const unsigned long long* __restrict__ counts,
-                                                            float* __restrict__ centroids, int64_t n, int G) {
+                                                            float* __restrict__ centroids, int64_t n, int G,
+                                                            const unsigned long long* __restrict__ overflow) {
+    const bool bad = *overflow != 0ull;
     for (int64_t i = (int64_t)blockIdx.x * kEncThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kEncThreads) {
+        if (bad) {
+            centroids[i] = __builtin_nanf("");
+            continue;
+        }
         const unsigned long long c = counts[i / G];
         if (c == 0) continue;
         const double sum = (double)(long long)sums[i] * kInvFixedPoint;
@@ -239,6 +252,12 @@ hipError_t kmeans_g(const EncArgs& a, const int64_t* seeds, void* workspace, int
     unsigned long long* sums = static_cast<unsigned long long*>(workspace);
     unsigned long long* counts = sums + (size_t)K * G;
     float* centroids = reinterpret_cast<float*>(counts + K);
+    // the flag sits after the centroids, 8-byte aligned (K G floats, K = 2^B >= 2)
+    unsigned long long* overflow = reinterpret_cast<unsigned long long*>(centroids + (size_t)K * G);
+    // targets below lim keep every coordinate sum over the n groups below 2^29 in magnitude,
+    // i.e. below 2^53 grid units: exact as int64 and in its float64 conversion
+    const float lim = (float)(536870912.0 / (double)(n > 0 ? n : 1));
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(kEncThreads), 0, stream, overflow, (int64_t)1);
     for (int m = 0; m < a.M; ++m) {
         hipLaunchKernelGGL((seed_kernel<G, CB>), dim3(grid_for(K, kEncThreads)), dim3(kEncThreads), 0, stream,
                            a.w, a.scales, a.codebooks, a.codes, seeds, centroids, n, gpr, (int)a.in, a.M, a.B, m);
@@ -260,14 +279,14 @@ hipError_t kmeans_g(const EncArgs& a, const int64_t* seeds, void* workspace, int
                 const int64_t cap = device_cu_count() * per_cu;
                 hipLaunchKernelGGL(kern, dim3((unsigned)(need < cap ? need : cap)), dim3(kEncThreads), lacc_bytes,
                                    stream, a.w, a.scales, a.codebooks, a.codes, centroids, sums, counts, n, gpr,
-                                   (int)a.in, a.M, a.B, m);
+                                   (int)a.in, a.M, a.B, m, lim, overflow);
             } else {
                 hipLaunchKernelGGL((assign_kernel<G, CB, true>), dim3(grid_for(n, kEncThreads)), dim3(kEncThreads),
                                    0, stream, a.w, a.scales, a.codebooks, a.codes, centroids, sums, counts, n, gpr,
-                                   (int)a.in, a.M, a.B, m);
+                                   (int)a.in, a.M, a.B, m, lim, overflow);
             }
             hipLaunchKernelGGL(update_kernel, dim3(grid_for((int64_t)K * G, kEncThreads)), dim3(kEncThreads), 0, stream,
-                               sums, counts, centroids, (int64_t)K * G, G);
+                               sums, counts, centroids, (int64_t)K * G, G, overflow);
         }
         hipLaunchKernelGGL(round_kernel, dim3(grid_for((int64_t)K * G, kEncThreads)), dim3(kEncThreads), 0, stream,
                            centroids, a.codebooks + ((size_t)m << a.B) * G, (int64_t)K * G);
@@ -293,7 +312,7 @@ hipError_t kmeans_g(const EncArgs& a, const int64_t* seeds, void* workspace, int
 int64_t kmeans_workspace_bytes(int M, int B, int g) {
     (void)M;
     const int64_t K = (int64_t)1 << B;
-    return K * g * 8 + K * 8 + K * g * 4;   // fixed-point sums, counts, fp32 centroids
+    return K * g * 8 + K * 8 + K * g * 4 + 16;   // fixed-point sums, counts, fp32 centroids, overflow flag
 }
 
 hipError_t launch_encode_greedy(const void* w, const void* scales, const void* codebooks, void* codes, int M, int B,

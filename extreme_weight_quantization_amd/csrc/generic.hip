@@ -127,8 +127,10 @@ __global__ __launch_bounds__(1024) void decode_generic_kernel(const uint8_t* __r
         cb = cbl;
     }
     const uint32_t mask = (1u << B) - 1u;
-    const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < n_units; u += stride) {
+    // 64-bit loop index: n_units may come within a stride of 2^32 (see decode_kernel)
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t u64 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u64 < n_units; u64 += stride) {
+        const uint32_t u = (uint32_t)u64;
         if constexpr (KG > 1) {
             static_assert(G * KG == 8, "one 16-byte store per unit");
             const uint32_t gid0 = u * KG;
@@ -199,7 +201,8 @@ __global__ __launch_bounds__(kGemvGenericThreads) void gemv_generic_kernel(const
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_grp = in / G;
     constexpr int kRows = kGemvGenericThreads / 64;
-    for (int row = blockIdx.x * kRows + wave; row < out; row += gridDim.x * kRows) {
+    // 64-bit row index: out may come within a grid stride of 2^31
+    for (int64_t row = (int64_t)blockIdx.x * kRows + wave; row < out; row += (int64_t)gridDim.x * kRows) {
         float acc[kGemvMaxBatchGeneric];
 #pragma unroll
         for (int b = 0; b < kGemvMaxBatchGeneric; ++b) acc[b] = 0.f;

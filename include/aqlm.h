@@ -193,10 +193,14 @@ int aqlm_kmeans_workspace_bytes(int M, int B, int g, int64_t* bytes);
  * A centroid is the mean of its members, summed exactly as integers in units
  * of 2^-24 and divided in float64, then rounded to fp32; an empty cluster
  * keeps its centroid; codebook m is the fp16 rounding of the centroids.  The
- * sums stay exact while a cluster's coordinate sum is below 2^29 in
- * magnitude (e.g. |W/s| < 256 with up to 2^21 groups).  `workspace` is
- * caller-owned device memory of at least aqlm_kmeans_workspace_bytes bytes
- * (16-byte aligned); its contents on entry do not matter.
+ * sums are exact while every target satisfies |W/s| < 2^29 / n_groups
+ * (n_groups = out * in / g; e.g. |W/s| < 256 with 2^21 groups).  A target at
+ * or above that bound, or not finite, cannot be summed exactly: the call then
+ * does not produce wrapped sums but NaN codebooks (from the first k-means round
+ * that meets such a target on; every later codebook too), and the codes
+ * assigned against them are 0.  `workspace` is caller-owned device memory of
+ * at least aqlm_kmeans_workspace_bytes bytes (16-byte aligned); its contents
+ * on entry do not matter.
  */
 int aqlm_kmeans_init(const void* w, const void* scales, const int64_t* seeds, void* codebooks, void* codes,
                      void* workspace, int64_t workspace_bytes, int M, int B, int g,

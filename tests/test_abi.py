@@ -172,12 +172,12 @@ def test_kmeans_workspace_bytes(lib):
     import ctypes as C
     n = C.c_int64(0)
     assert lib.aqlm_kmeans_workspace_bytes(2, 8, 8, C.byref(n)) == binding.AQLM_OK
-    assert n.value == 256 * 8 * 8 + 256 * 8 + 256 * 8 * 4       # int64 sums, int64 counts, fp32 centroids
+    assert n.value == 256 * 8 * 8 + 256 * 8 + 256 * 8 * 4 + 16   # int64 sums, int64 counts, fp32 centroids, flag
     assert lib.aqlm_kmeans_workspace_bytes(1, 16, 8, C.byref(n)) == binding.AQLM_OK
-    assert n.value == 65536 * (8 * 12 + 8)
+    assert n.value == 65536 * (8 * 12 + 8) + 16
     assert lib.aqlm_kmeans_workspace_bytes(2, 17, 8, C.byref(n)) == binding.AQLM_ERR_SCHEME
     assert lib.aqlm_kmeans_workspace_bytes(2, 8, 8, None) == binding.AQLM_ERR_NULL
-    assert binding.kmeans_workspace_bytes(4, 8, 16) == 256 * (16 * 12 + 8)
+    assert binding.kmeans_workspace_bytes(4, 8, 16) == 256 * (16 * 12 + 8) + 16
 
 
 def test_validation_encode(lib):

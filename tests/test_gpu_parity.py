@@ -632,6 +632,29 @@ def test_kmeans_init_bit_exact_members_near_the_fixed_point_grid():
     np.testing.assert_array_equal(codes.cpu().numpy(), codes_ref)
 
 
+def test_kmeans_init_out_of_range_targets_give_nan_codebooks():
+    """Scales of 2^-14 make |W/s| reach 2^13, above the exact-sum bound 2^29 / n_groups (2^29 / 2^17
+    groups = 2^12): the codebooks come out NaN and the codes 0 instead of wrapped sums.  The same
+    weights with unit scales stay in range and match the oracle."""
+    rng = np.random.default_rng(22)
+    out, n_in, B, g = 2048, 512, 6, 8          # 2^17 groups
+    w = (rng.normal(0, 0.25, size=(out, n_in))).astype(np.float16)
+    seeds = rng.choice(out * n_in // g, (1, 1 << B), replace=False).astype(np.int64)
+    tiny = np.full(out, 2.0 ** -14, np.float16)
+    cb, codes = E.aqlm_kmeans_init(torch.from_numpy(w).cuda(), torch.from_numpy(tiny).cuda(),
+                                   torch.from_numpy(seeds).cuda(), B, g, 2)
+    torch.cuda.synchronize()
+    assert np.isnan(cb.cpu().numpy().astype(np.float32)).all()
+    assert not codes.cpu().numpy().any()
+    ones = np.ones(out, np.float16)
+    cb, codes = E.aqlm_kmeans_init(torch.from_numpy(w).cuda(), torch.from_numpy(ones).cuda(),
+                                   torch.from_numpy(seeds).cuda(), B, g, 2)
+    torch.cuda.synchronize()
+    cb_ref, codes_ref = O.kmeans_residual_init(w, ones, seeds, 1, B, g, 2)
+    np.testing.assert_array_equal(cb.cpu().numpy().view(np.uint16), cb_ref.view(np.uint16))
+    np.testing.assert_array_equal(codes.cpu().numpy(), codes_ref)
+
+
 def test_encode_and_kmeans_full_size_2x8():
     """4096x4096 weights: encoder codes on sampled rows equal the oracle's; the k-means codes are the
     greedy encoding against the k-means codebooks (checked on sampled rows)."""
@@ -670,3 +693,26 @@ def test_binding_errors_on_gpu():
         E.aqlm_linear_gemv(codes, cb, s, x[:, :128])
     y0 = E.aqlm_linear_gemm(codes, cb, s, torch.zeros((0, 256), dtype=torch.float16, device="cuda"))
     assert y0.shape == (0, 64)
+    # shapes that would make a kernel read past a buffer are refused on the host, before any launch
+    one_code = codes[:, :, :1].contiguous()                 # uint8 [out][G][1] with 2x8 codebooks
+    for fn in (E.aqlm_linear_gemv, E.aqlm_linear_gemm, E.aqlm_linear_gemm_dequant):
+        with pytest.raises(ValueError, match="codebooks"):
+            fn(one_code, cb, s, x)
+        with pytest.raises(ValueError, match="scales"):
+            fn(codes, cb, s[:32].contiguous(), x)         # 32 scales for 64 rows
+    with pytest.raises(ValueError, match="codebooks"):
+        E.aqlm_linear_decode(one_code, cb, s)
+    with pytest.raises(ValueError, match="scales"):
+        E.aqlm_linear_decode(codes, cb, s[:63].contiguous())
+    with pytest.raises(ValueError, match="scales"):
+        E.aqlm_linear_gemv_fused([(codes, cb, s), (codes, cb, s[:10].contiguous())], x)
+    with pytest.raises(ValueError, match="codebooks"):
+        E.aqlm_linear_gemv_fused([(codes, cb, s), (one_code, cb, s)], x)
+    L16 = synth.make_layer("1x16", 64, 256, batch=1, seed=1)
+    c16, cb16, s16, x16 = dev(L16)
+    lists = E.aqlm_lists_pack(c16)
+    with pytest.raises(ValueError, match="scales"):
+        E.aqlm_linear_gemv_lists(lists, cb16, s16[:8].contiguous(), x16)
+    with pytest.raises(ValueError, match="scales"):
+        E.aqlm_linear_gemv_lists_fused([(lists, cb16, s16[:8].contiguous())], x16)
+    torch.cuda.synchronize()
