@@ -40,6 +40,16 @@ namespace aqlm {
 
 namespace {
 
+// One IEEE operation each, rounded to nearest-even, never fused with a neighbour.
+// The runtime's rounded-operation intrinsics are plain operators in its own header,
+// where contraction is allowed, so after inlining a product feeding a sum became a
+// fused multiply-add (one rounding instead of two) and moved distance ties.  These
+// are defined under this file's contract(off).
+__device__ __forceinline__ float add_rn(float a, float b) { return a + b; }
+__device__ __forceinline__ float sub_rn(float a, float b) { return a - b; }
+__device__ __forceinline__ float mul_rn(float a, float b) { return a * b; }
+__device__ __forceinline__ float div_rn(float a, float b) { return a / b; }
+
 constexpr int kEncThreads = 256;
 constexpr int kTileBytes = 32768;
 constexpr double kFixedPoint = 16777216.0;          // 2^24
@@ -69,13 +79,13 @@ __device__ __forceinline__ void residual(const f16* __restrict__ w, const f16* _
     const float s = (float)scales[row];
     const f16* src = w + row * in + j * G;
 #pragma unroll
-    for (int t = 0; t < G; ++t) r[t] = __fdiv_rn((float)src[t], s);
+    for (int t = 0; t < G; ++t) r[t] = div_rn((float)src[t], s);
     const uint32_t mask = (1u << B) - 1u;
     for (int mm = 0; mm < m; ++mm) {
         const uint32_t k = load_code<CB>(codes, (size_t)n * M + mm, mask);
         const f16* c = codebooks + (((size_t)mm << B) + k) * G;
 #pragma unroll
-        for (int t = 0; t < G; ++t) r[t] = __fsub_rn(r[t], (float)c[t]);
+        for (int t = 0; t < G; ++t) r[t] = sub_rn(r[t], (float)c[t]);
     }
 }
 
@@ -123,8 +133,8 @@ __global__ __launch_bounds__(kEncThreads) void assign_kernel(
                     float d = 0.f;
 #pragma unroll
                     for (int t = 0; t < G; ++t) {
-                        const float e = __fsub_rn(r[t], tile[k * G + t]);
-                        d = __fadd_rn(d, __fmul_rn(e, e));
+                        const float e = sub_rn(r[t], tile[k * G + t]);
+                        d = add_rn(d, mul_rn(e, e));
                     }
                     if (d < best) {
                         best = d;
