@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     SliceLists,
     aqlm_linear_gemv_lists,
     aqlm_linear_gemv_lists_fused,
+    aqlm_linear_gemv_lists_noalloc,
     aqlm_lists_pack,
     aqlm_linear_decode,
     aqlm_linear_gemm,

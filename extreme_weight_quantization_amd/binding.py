@@ -16,12 +16,12 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaqlm.so")
 
-AQLM_OK, AQLM_ERR_NULL, AQLM_ERR_SHAPE, AQLM_ERR_SCHEME, AQLM_ERR_ALIGN, AQLM_ERR_HIP = range(6)
+AQLM_OK, AQLM_ERR_NULL, AQLM_ERR_SHAPE, AQLM_ERR_SCHEME, AQLM_ERR_ALIGN, AQLM_ERR_HIP, AQLM_ERR_SCRATCH = range(7)
 EXPORTED = ("aqlm_linear_gemv", "aqlm_linear_gemv_fused", "aqlm_linear_gemm", "aqlm_linear_decode",
             "aqlm_encode_greedy", "aqlm_kmeans_workspace_bytes", "aqlm_kmeans_init",
             "aqlm_lists_table_bytes", "aqlm_lists_workspace_bytes", "aqlm_lists_plan", "aqlm_lists_fill",
             "aqlm_linear_gemv_lists", "aqlm_linear_gemv_lists_fused", "aqlm_lists_fused_workspace_bytes",
-            "aqlm_linear_gemm_dequant", "aqlm_gemm_dequant_workspace_bytes",
+            "aqlm_linear_gemm_dequant", "aqlm_gemm_dequant_workspace_bytes", "aqlm_linear_gemv_lists_noalloc",
             "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
 FUSED_MAX_LAYERS = 8   # AQLM_FUSED_MAX_LAYERS
 
@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.aqlm_lists_fill.restype = ci
         lib.aqlm_linear_gemv_lists.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, ci, ci, ci, i64, i64, i64, vp]
         lib.aqlm_linear_gemv_lists.restype = ci
+        lib.aqlm_linear_gemv_lists_noalloc.argtypes = [vp, vp, i64, vp, vp, vp, vp, ci, ci, ci, i64, i64, i64, vp]
+        lib.aqlm_linear_gemv_lists_noalloc.restype = ci
         lib.aqlm_linear_gemv_lists_fused.argtypes = [ci, pp, pp, ctypes.POINTER(i64), pp, pp, ctypes.POINTER(i64),
                                                      vp, pp, vp, i64, ci, ci, ci, i64, i64, vp]
         lib.aqlm_linear_gemv_lists_fused.restype = ci
@@ -428,6 +430,32 @@ def aqlm_linear_gemv_lists(lists: SliceLists, codebooks, scales, x, y=None, work
         _ptr(lists.table), _ptr(lists.entries), lists.entries.numel(), _ptr(codebooks), _ptr(scales), _ptr(x),
         _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(), 1, 16, 8, lists.out, lists.n_in,
         batch, _stream(x.device)))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20   # AQLM_LISTS_NOALLOC_SCRATCH_BYTES
+
+
+def aqlm_linear_gemv_lists_noalloc(lists: SliceLists, codebooks, scales, x, y):
+    """aqlm_linear_gemv_lists with the partial sums in the library's static scratch (see aqlm.h).
+
+    y must be given: the call allocates nothing.  Calls that overlap on one GPU race."""
+    for name, t in (("codebooks", codebooks), ("scales", scales), ("x", x), ("y", y)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float16:
+            raise ValueError(f"{name} must be a contiguous float16 GPU tensor")
+    if codebooks.shape != (1, 1 << 16, 8):
+        raise ValueError("codebooks must be [1][65536][8]")
+    if x.dim() != 2 or x.shape[1] != lists.n_in or x.shape[0] > 1:
+        raise ValueError(f"x must be [1][{lists.n_in}]")
+    if scales.shape != (lists.out,):
+        raise ValueError(f"scales must be [{lists.out}] (one per output row)")
+    if y.shape != (x.shape[0], lists.out):
+        raise ValueError(f"y must be [{x.shape[0]}][{lists.out}]")
+    _same_device((("table", lists.table), ("entries", lists.entries), ("codebooks", codebooks), ("scales", scales),
+                  ("x", x), ("y", y)))
+    _check(load_library().aqlm_linear_gemv_lists_noalloc(
+        _ptr(lists.table), _ptr(lists.entries), lists.entries.numel(), _ptr(codebooks), _ptr(scales), _ptr(x),
+        _ptr(y), 1, 16, 8, lists.out, lists.n_in, int(x.shape[0]), _stream(x.device)))
     return y
 
 

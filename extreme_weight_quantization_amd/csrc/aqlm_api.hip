@@ -311,6 +311,27 @@ int aqlm_linear_gemv_lists(const void* table, const void* entries, int64_t entri
                                     (hipStream_t)stream));
 }
 
+static_assert(AQLM_LISTS_NOALLOC_SCRATCH_BYTES == kListsScratchBytes, "scratch size");
+
+int aqlm_linear_gemv_lists_noalloc(const void* table, const void* entries, int64_t entries_bytes,
+                                   const void* codebooks, const void* scales, const void* x, void* y, int M, int B,
+                                   int g, int64_t out, int64_t in, int64_t batch, void* stream) {
+    const int st = validate_lists(M, B, g, out, in);
+    if (st != AQLM_OK) return st;
+    if (batch < 0 || batch > 1 || entries_bytes < 0) return AQLM_ERR_SHAPE;
+    if (lists_workspace_bytes(out, in) > kListsScratchBytes) return AQLM_ERR_SCRATCH;
+    if (out == 0 || batch == 0) return AQLM_OK;
+    if (!table || !entries || !codebooks || !scales || !x || !y) return AQLM_ERR_NULL;
+    if (!aligned(table, 16) || !aligned(entries, 16) || !aligned(codebooks, 16) || !aligned(x, 16) ||
+        !aligned(y, 16) || !aligned(scales, 2))
+        return AQLM_ERR_ALIGN;
+    void* partial = nullptr;
+    const hipError_t e = lists_scratch(&partial);
+    if (e != hipSuccess) return finish(e);
+    return finish(launch_gemv_lists(table, entries, entries_bytes, codebooks, scales, x, y, partial, out, in,
+                                    (hipStream_t)stream));
+}
+
 int aqlm_lists_fused_workspace_bytes(int n_layers, const int64_t* outs, int M, int B, int g, int64_t in,
                                      int64_t* bytes) {
     if (!bytes || !outs) return AQLM_ERR_NULL;
@@ -372,6 +393,9 @@ const char* aqlm_status_str(int status) {
         case AQLM_ERR_SCHEME: return "AQLM_ERR_SCHEME: need 1 <= M <= 8, 1 <= B <= 16, g in {1,2,4,8,16,32}";
         case AQLM_ERR_ALIGN: return "AQLM_ERR_ALIGN: codes/codebooks/x/y need 16-byte, scales 2-byte alignment";
         case AQLM_ERR_HIP: return "AQLM_ERR_HIP: HIP runtime error at launch (see aqlm_last_hip_error)";
+        case AQLM_ERR_SCRATCH:
+            return "AQLM_ERR_SCRATCH: the problem needs more scratch than the allocation-free entry point's "
+                   "static buffer holds (AQLM_LISTS_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown aqlm status";
     }
 }

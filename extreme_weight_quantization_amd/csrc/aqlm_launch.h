@@ -123,5 +123,9 @@ hipError_t launch_lists_fill(const void* codes, int64_t out, int64_t in, const v
 hipError_t launch_gemv_lists(const void* table, const void* entries, int64_t entries_bytes, const void* codebook,
                              const void* scales, const void* x, void* y, void* workspace, int64_t out, int64_t in,
                              hipStream_t stream);
+// Bytes of the static scratch array of the allocation-free slice-list product.
+constexpr int64_t kListsScratchBytes = (int64_t)4 << 20;
+// This device's address of that array (looked up once per device; thread-safe).
+hipError_t lists_scratch(void** ptr);
 
 }  // namespace aqlm

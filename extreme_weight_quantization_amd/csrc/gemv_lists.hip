@@ -36,11 +36,19 @@
 // adds a row's 8 J partials in a fixed order, applies the scale and rounds to
 // fp16 once.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
 namespace aqlm {
+
+// Scratch of the allocation-free product (aqlm_linear_gemv_lists_noalloc): the fp32
+// partial sums of one layer, kListsScratchBytes at most.  Every GPU holds its own copy
+// for the life of the process.  In host code `scratch` only names the symbol; its
+// device address comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) float scratch[kListsScratchBytes / 4];
 
 namespace {
 
@@ -505,6 +513,32 @@ hipError_t launch_gemv_lists_fused(ListsLayers L, const void* x, int64_t in, hip
                            static_cast<f16*>(L.y[0]), L.out[0], g.n_rt * 64, g.slots());
     }
     return hipGetLastError();
+}
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t lists_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with this device current
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_gemv_lists(const void* table, const void* entries, int64_t entries_bytes, const void* codebook,

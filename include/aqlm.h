@@ -64,7 +64,8 @@ typedef enum {
     AQLM_ERR_SHAPE = 2,  /* out/in/batch negative or out of range, in % g != 0 */
     AQLM_ERR_SCHEME = 3, /* (M, B, g) outside 1..AQLM_MAX_CODEBOOKS x 1..16 x {1,2,4,8,16,32} */
     AQLM_ERR_ALIGN = 4,  /* codes, codebooks, x or y not 16-byte aligned, scales not 2-byte aligned */
-    AQLM_ERR_HIP = 5     /* the HIP runtime reported an error at launch */
+    AQLM_ERR_HIP = 5,    /* the HIP runtime reported an error at launch */
+    AQLM_ERR_SCRATCH = 6 /* more scratch needed than an allocation-free entry point holds */
 } aqlm_status;
 
 /* Largest `in` accepted (inputs per row). */
@@ -280,6 +281,26 @@ int aqlm_linear_gemv_lists_fused(int n_layers, const void* const* tables, const 
 /* Bytes of workspace aqlm_linear_gemv_lists_fused needs for the layers' outs (host array). */
 int aqlm_lists_fused_workspace_bytes(int n_layers, const int64_t* outs, int M, int B, int g, int64_t in,
                                      int64_t* bytes);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): aqlm_linear_gemv_lists
+ * without the workspace argument.  The fp32 partial sums go to a static device
+ * array of the library, AQLM_LISTS_NOALLOC_SCRATCH_BYTES long, that every GPU the
+ * library runs on holds until the process ends; the call allocates and frees
+ * nothing (its first call on a device looks the array's address up once).  A
+ * layer whose partial sums (aqlm_lists_workspace_bytes) exceed the array gives
+ * AQLM_ERR_SCRATCH and enqueues nothing; 4 MiB covers e.g. every Llama-2-7B and
+ * 70B projection.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  Each call writes every partial it reads, so the
+ * array needs no clearing between calls.  Other arguments, validation and
+ * results are those of aqlm_linear_gemv_lists (bit-identical to it).
+ */
+#define AQLM_LISTS_NOALLOC_SCRATCH_BYTES (4 << 20)
+int aqlm_linear_gemv_lists_noalloc(const void* table, const void* entries, int64_t entries_bytes,
+                                   const void* codebooks, const void* scales, const void* x, void* y, int M, int B,
+                                   int g, int64_t out, int64_t in, int64_t batch, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* aqlm_status_str(int status);

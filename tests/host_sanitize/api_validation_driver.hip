@@ -66,6 +66,11 @@ hipError_t launch_lists_fill(const void*, int64_t, int64_t, const void*, void*, 
 }
 hipError_t launch_gemv_lists(const void*, const void*, int64_t, const void*, const void*, const void*, void*,
                              void*, int64_t, int64_t, hipStream_t) { return stub(); }
+hipError_t lists_scratch(void** ptr) {
+    static float fake[16];
+    *ptr = fake;
+    return hipSuccess;
+}
 }  // namespace aqlm
 
 #define CHECK(expr, want_status, want_launches)                                                        \
@@ -204,6 +209,17 @@ int main() {
     CHECK(aqlm_linear_gemv_lists(ws, y, 4096, cb, s, x, y, ws, 64 * 32, 1, 16, 8, 64, 256, 2, st), AQLM_ERR_SHAPE, 0);
     CHECK(aqlm_linear_gemv_lists(ws, y, I64_MIN, cb, s, x, y, ws, 64 * 32, 1, 16, 8, 64, 256, 1, st),
           AQLM_ERR_SHAPE, 0);
+    // allocation-free variant: the stub's lists_workspace_bytes is out * 32, so 131072 rows fill 4 MiB
+    CHECK(aqlm_linear_gemv_lists_noalloc(ws, y, 4096, cb, s, x, y, 1, 16, 8, 64, 256, 1, st), AQLM_OK, 1);
+    CHECK(aqlm_linear_gemv_lists_noalloc(ws, y, 4096, cb, s, x, y, 1, 16, 8, 131072, 256, 1, st), AQLM_OK, 1);
+    CHECK(aqlm_linear_gemv_lists_noalloc(ws, y, 4096, cb, s, x, y, 1, 16, 8, 131073, 256, 1, st),
+          AQLM_ERR_SCRATCH, 0);
+    CHECK(aqlm_linear_gemv_lists_noalloc(ws, y, 4096, cb, s, x, nullptr, 1, 16, 8, 64, 256, 1, st), AQLM_ERR_NULL, 0);
+    CHECK(aqlm_linear_gemv_lists_noalloc(ws, y, 4096, cb, s, x, odd, 1, 16, 8, 64, 256, 1, st), AQLM_ERR_ALIGN, 0);
+    CHECK(aqlm_linear_gemv_lists_noalloc(ws, y, 4096, cb, s, x, y, 2, 8, 8, 64, 256, 1, st), AQLM_ERR_SCHEME, 0);
+    CHECK(aqlm_linear_gemv_lists_noalloc(nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, 1, 16, 8, 0, 256,
+                                         1, st), AQLM_OK, 0);
+    CHECK(aqlm_linear_gemv_lists_noalloc(ws, y, I64_MIN, cb, s, x, y, 1, 16, 8, 64, 256, 1, st), AQLM_ERR_SHAPE, 0);
     for (int n = 1; n <= AQLM_FUSED_MAX_LAYERS; ++n) {
         const void** t = static_cast<const void**>(malloc(n * sizeof(void*)));
         const void** e = static_cast<const void**>(malloc(n * sizeof(void*)));

@@ -47,7 +47,7 @@ def test_exports_are_plain_c_symbols():
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert binding.status_str(s).startswith("AQLM_")
     assert "unknown" in binding.status_str(99)
     assert lib.aqlm_version().decode().count(".") == 2
