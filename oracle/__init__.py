@@ -16,4 +16,9 @@ from .aqlm_oracle import (  # noqa: F401
     bits_per_weight_terms,
     parity_errors,
     within_tolerance,
+    pack_codes,
+    unpack_codes,
+    packed_words,
+    packed_to_stored,
+    decode_fp32_packed,
 )

@@ -150,6 +150,55 @@ def decode_loop(codes, codebooks, scales) -> np.ndarray:
     return w
 
 
+# ---------------------------------------------------------------------------
+# Bit-packed codes
+#
+# "Key AQLM quantization parameters": a B that is not a multiple of 8 leaves
+# unused bits in the bytes that hold each code.  The packed storage drops them.
+# Reading (the pages give no packed layout): the codes in their stored order
+# ([out][in/g][M] flattened, code n = (i * G + j) * M + m) form one bit stream,
+# code n in bits [n * B, n * B + B), least significant bit first; bit b of the
+# stream is bit b % 32 of 32-bit word b // 32 (words little-endian), and the
+# stream is padded with zero bits to a whole number of words.  Rows are not
+# padded, so a row may start inside a word.
+
+
+def packed_words(n_codes: int, B: int) -> int:
+    """Number of 32-bit words that hold n_codes codes of B bits."""
+    return (n_codes * B + 31) // 32
+
+
+def pack_codes(codes: np.ndarray, B: int) -> np.ndarray:
+    """The uint32 word stream of the codes' indices (low B bits), code after code, LSB first."""
+    idx = codes_to_index(codes, B).reshape(-1)
+    bits = ((idx[:, None] >> np.arange(B, dtype=np.int64)[None, :]) & 1).astype(np.uint8).reshape(-1)
+    total = packed_words(idx.size, B) * 32
+    stream = np.zeros(total, np.uint8)
+    stream[:bits.size] = bits
+    return np.packbits(stream, bitorder="little").view("<u4").astype(np.uint32)
+
+
+def unpack_codes(words: np.ndarray, B: int, shape) -> np.ndarray:
+    """Indices (int64, shape) of the codes in a packed word stream."""
+    n = int(np.prod(shape))
+    if words.size < packed_words(n, B):
+        raise ValueError("the word stream is shorter than the codes it should hold")
+    stream = np.unpackbits(np.ascontiguousarray(words, dtype="<u4").view(np.uint8), bitorder="little")
+    bits = stream[:n * B].reshape(n, B).astype(np.int64)
+    return (bits << np.arange(B, dtype=np.int64)[None, :]).sum(1).reshape(shape)
+
+
+def packed_to_stored(words, M, B, g, out, n_in) -> np.ndarray:
+    """The whole-byte code array [out][in/g][M] that a packed stream encodes."""
+    idx = unpack_codes(words, B, (out, n_in // g, M))
+    return idx.astype(np.uint8) if B <= 8 else idx.astype(np.uint16).view(np.int16)
+
+
+def decode_fp32_packed(words, codebooks, scales, M, B, g, out, n_in, rows=None) -> np.ndarray:
+    """decode_fp32 of the layer whose codes are the packed stream `words`."""
+    return decode_fp32(packed_to_stored(words, M, B, g, out, n_in), codebooks, scales, rows)
+
+
 def linear_ref_f64(codes, codebooks, scales, x) -> np.ndarray:
     """y[b][i] = sum_k W[i][k] * x[b][k] in float64, W from ``decode_fp32``.
 

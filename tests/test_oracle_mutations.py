@@ -59,8 +59,18 @@ ENCODE_MUTANTS = {
     "targets_times_scale": ("r = w.astype(np.float32) / scales.astype(np.float32)[:, None]",
                             "r = w.astype(np.float32) * scales.astype(np.float32)[:, None]"),
 }
+# Mistakes in the bit-packed codes, caught by test_oracle_packed.py.
+PACKED_MUTANTS = {
+    "pack_msb_first": ("bits = ((idx[:, None] >> np.arange(B, dtype=np.int64)[None, :]) & 1)",
+                       "bits = ((idx[:, None] >> np.arange(B - 1, -1, -1, dtype=np.int64)[None, :]) & 1)"),
+    "pack_big_endian_bits": ('return np.packbits(stream, bitorder="little")', 'return np.packbits(stream, bitorder="big")'),
+    "pack_codebook_major": ("idx = codes_to_index(codes, B).reshape(-1)",
+                            "idx = np.moveaxis(codes_to_index(codes, B), -1, 0).reshape(-1)"),
+    "pack_one_bit_short": ("total = packed_words(idx.size, B) * 32", "total = packed_words(idx.size, B - 1) * 32"),
+}
 CASES = [(n, MUTANTS[n], "test_oracle.py") for n in sorted(MUTANTS)] + \
-        [(n, ENCODE_MUTANTS[n], "test_oracle_encode.py") for n in sorted(ENCODE_MUTANTS)]
+        [(n, ENCODE_MUTANTS[n], "test_oracle_encode.py") for n in sorted(ENCODE_MUTANTS)] + \
+        [(n, PACKED_MUTANTS[n], "test_oracle_packed.py") for n in sorted(PACKED_MUTANTS)]
 
 
 @pytest.mark.parametrize("name,mutant,pins", CASES, ids=[c[0] for c in CASES])
