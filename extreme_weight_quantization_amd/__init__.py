@@ -11,6 +11,11 @@ from .binding import (  # noqa: F401
     aqlm_linear_gemv_lists,
     aqlm_linear_gemv_lists_fused,
     aqlm_linear_gemv_lists_noalloc,
+    aqlm_pack_codes,
+    aqlm_linear_gemv_packed,
+    aqlm_linear_gemm_packed,
+    aqlm_linear_decode_packed,
+    packed_codes_bytes,
     aqlm_lists_pack,
     aqlm_linear_decode,
     aqlm_linear_gemm,

@@ -22,6 +22,8 @@ EXPORTED = ("aqlm_linear_gemv", "aqlm_linear_gemv_fused", "aqlm_linear_gemm", "a
             "aqlm_lists_table_bytes", "aqlm_lists_workspace_bytes", "aqlm_lists_plan", "aqlm_lists_fill",
             "aqlm_linear_gemv_lists", "aqlm_linear_gemv_lists_fused", "aqlm_lists_fused_workspace_bytes",
             "aqlm_linear_gemm_dequant", "aqlm_gemm_dequant_workspace_bytes", "aqlm_linear_gemv_lists_noalloc",
+            "aqlm_packed_codes_bytes", "aqlm_pack_codes", "aqlm_linear_gemv_packed", "aqlm_linear_gemm_packed",
+            "aqlm_linear_decode_packed",
             "aqlm_status_str", "aqlm_last_hip_error", "aqlm_version")
 FUSED_MAX_LAYERS = 8   # AQLM_FUSED_MAX_LAYERS
 
@@ -46,7 +48,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                "`python -m extreme_weight_quantization_amd.build`")
         lib = ctypes.CDLL(path)
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-        for name in ("aqlm_linear_gemv", "aqlm_linear_gemm", "aqlm_linear_decode"):
+        for name in ("aqlm_linear_gemv", "aqlm_linear_gemm", "aqlm_linear_decode", "aqlm_linear_gemv_packed",
+                     "aqlm_linear_gemm_packed", "aqlm_linear_decode_packed"):
             fn = getattr(lib, name)
             fn.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, i64, i64, i64, vp]
             fn.restype = ci
@@ -81,6 +84,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.aqlm_linear_gemm_dequant.restype = ci
         lib.aqlm_gemm_dequant_workspace_bytes.argtypes = [ci, ci, ci, i64, i64, ctypes.POINTER(i64)]
         lib.aqlm_gemm_dequant_workspace_bytes.restype = ci
+        lib.aqlm_packed_codes_bytes.argtypes = [ci, ci, ci, i64, i64, ctypes.POINTER(i64)]
+        lib.aqlm_packed_codes_bytes.restype = ci
+        lib.aqlm_pack_codes.argtypes = [vp, vp, ci, ci, ci, i64, i64, vp]
+        lib.aqlm_pack_codes.restype = ci
         lib.aqlm_status_str.argtypes = [ci]
         lib.aqlm_status_str.restype = ctypes.c_char_p
         lib.aqlm_last_hip_error.argtypes = []
@@ -282,6 +289,96 @@ def aqlm_linear_decode(codes, codebooks, scales, w=None):
     _same_device((("codes", codes), ("w", w)))
     _check(load_library().aqlm_linear_decode(_ptr(codes), _ptr(codebooks), _ptr(scales), None,
                                              _ptr(w), M, B, g, out, G * g, 0, _stream(codes.device)))
+    return w
+
+
+# ---------------------------------------------------------------------------
+# Bit-packed codes (layout in aqlm.h): an int32 tensor holds the 32-bit words.
+
+
+def packed_codes_bytes(M: int, B: int, g: int, out: int, n_in: int) -> int:
+    """Bytes of the bit-packed codes of a layer [out][n_in] of scheme (M, B, g)."""
+    n = ctypes.c_int64(0)
+    _check(load_library().aqlm_packed_codes_bytes(M, B, g, out, n_in, ctypes.byref(n)))
+    return int(n.value)
+
+
+def aqlm_pack_codes(codes, B: int, packed=None):
+    """The bit-packed stream (int32 words) of whole-byte codes [out][in/g][M] whose indices have B bits."""
+    if not (codes.is_cuda and codes.is_contiguous() and codes.dim() == 3):
+        raise ValueError("codes must be a contiguous GPU tensor [out][in/g][M]")
+    if (B <= 8) != (codes.dtype == torch.uint8) or codes.dtype not in (torch.uint8, torch.int16):
+        raise ValueError("codes must be uint8 for B <= 8 and int16 for 9 <= B <= 16")
+    out, G, M = (int(v) for v in codes.shape)
+    n_words = packed_codes_bytes(M, B, 1, out, G) // 4   # g = 1 with in = G: the same code count
+    if packed is None:
+        packed = torch.empty((max(n_words, 1),), dtype=torch.int32, device=codes.device)
+    elif packed.dtype != torch.int32 or not packed.is_contiguous() or packed.numel() < n_words:
+        raise ValueError(f"packed must be a contiguous int32 tensor of at least {n_words} words")
+    _same_device((("codes", codes), ("packed", packed)))
+    _check(load_library().aqlm_pack_codes(_ptr(codes), _ptr(packed), M, B, 1, out, G, _stream(codes.device)))
+    return packed
+
+
+def _packed_args(packed, codebooks, scales, n_in, x=None):
+    for name, t in (("packed", packed), ("codebooks", codebooks), ("scales", scales), ("x", x)):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    _same_device((("packed", packed), ("codebooks", codebooks), ("scales", scales), ("x", x)))
+    if packed.dtype != torch.int32:
+        raise ValueError("packed codes must be an int32 tensor of 32-bit words")
+    if codebooks.dtype != torch.float16 or scales.dtype != torch.float16 or codebooks.dim() != 3 or scales.dim() != 1:
+        raise ValueError("codebooks [M][2^B][g] and scales [out] must be float16")
+    M, K, g = (int(v) for v in codebooks.shape)
+    B = K.bit_length() - 1
+    if K != 1 << B:
+        raise ValueError("the codebook size must be a power of two")
+    out = int(scales.shape[0])
+    if n_in % g:
+        raise ValueError("in must be a multiple of g")
+    need = packed_codes_bytes(M, B, g, out, n_in)
+    if packed.numel() * 4 < need:
+        raise ValueError(f"packed holds {packed.numel() * 4} bytes, the layer needs {need}")
+    return M, B, g, out
+
+
+def _packed_linear(fn_name, packed, codebooks, scales, x, y):
+    if x.dtype != torch.float16 or x.dim() != 2:
+        raise ValueError("x must be float16 [batch][in]")
+    n_in, batch = int(x.shape[1]), int(x.shape[0])
+    M, B, g, out = _packed_args(packed, codebooks, scales, n_in, x)
+    if y is None:
+        y = torch.empty((batch, out), dtype=torch.float16, device=x.device)
+    elif y.shape != (batch, out) or y.dtype != torch.float16 or not y.is_contiguous():
+        raise ValueError(f"y must be a contiguous float16 [{batch}][{out}] tensor")
+    _same_device((("x", x), ("y", y)))
+    _check(getattr(load_library(), fn_name)(_ptr(packed), _ptr(codebooks), _ptr(scales), _ptr(x), _ptr(y), M, B, g,
+                                            out, n_in, batch, _stream(x.device)))
+    return y
+
+
+def aqlm_linear_gemv_packed(packed, codebooks, scales, x, y=None):
+    """y = W x at batch 1..16 with W's codes bit-packed (out = scales.shape[0], in = x.shape[1])."""
+    return _packed_linear("aqlm_linear_gemv_packed", packed, codebooks, scales, x, y)
+
+
+def aqlm_linear_gemm_packed(packed, codebooks, scales, x, y=None):
+    """Y = X W^T for any batch of tokens, W's codes bit-packed."""
+    return _packed_linear("aqlm_linear_gemm_packed", packed, codebooks, scales, x, y)
+
+
+def aqlm_linear_decode_packed(packed, codebooks, scales, n_in, w=None):
+    """W16[out][n_in] from bit-packed codes, bit-exact."""
+    M, B, g, out = _packed_args(packed, codebooks, scales, int(n_in))
+    if w is None:
+        w = torch.empty((out, int(n_in)), dtype=torch.float16, device=packed.device)
+    elif w.shape != (out, int(n_in)) or w.dtype != torch.float16 or not w.is_contiguous():
+        raise ValueError(f"w must be a contiguous float16 [{out}][{n_in}] tensor")
+    _same_device((("packed", packed), ("w", w)))
+    _check(load_library().aqlm_linear_decode_packed(_ptr(packed), _ptr(codebooks), _ptr(scales), None, _ptr(w), M, B,
+                                                    g, out, int(n_in), 0, _stream(packed.device)))
     return w
 
 

@@ -57,7 +57,7 @@ static int gemv_b8_scheme(int M, int B, int g, int64_t in, int64_t batch) {
 // scheme id, or an error status; touches no HIP state.
 static int validate(Op op, const void* codes, const void* codebooks, const void* scales,
                     const void* x, const void* y, int M, int B, int g, int64_t out, int64_t in,
-                    int64_t batch, int* scheme, bool* empty) {
+                    int64_t batch, int* scheme, bool* empty, uintptr_t codes_align = 16) {
     if (op == Op::kDecode && x != nullptr) return AQLM_ERR_NULL;
     if (M == 1 && B == 16 && g == 8) *scheme = kScheme1x16;
     else if (M == 2 && B == 8 && g == 8) *scheme = kScheme2x8;
@@ -77,7 +77,7 @@ static int validate(Op op, const void* codes, const void* codebooks, const void*
     if (*empty) return AQLM_OK;
     if (!codes || !codebooks || !scales || !y) return AQLM_ERR_NULL;
     if (op != Op::kDecode && x == nullptr) return AQLM_ERR_NULL;
-    if (!aligned(codes, 16) || !aligned(codebooks, 16) || !aligned(y, 16) || !aligned(scales, 2))
+    if (!aligned(codes, codes_align) || !aligned(codebooks, 16) || !aligned(y, 16) || !aligned(scales, 2))
         return AQLM_ERR_ALIGN;
     if (x && !aligned(x, 16)) return AQLM_ERR_ALIGN;
     return AQLM_OK;
@@ -161,6 +161,56 @@ int aqlm_linear_gemm(const void* codes, const void* codebooks, const void* scale
                                           batch, (hipStream_t)stream));
     return finish(launch_gemm(scheme, codes, codebooks, scales, x, y, out, in, batch,
                               (hipStream_t)stream));
+}
+
+// ---- bit-packed codes: every scheme, on the general kernels
+int aqlm_packed_codes_bytes(int M, int B, int g, int64_t out, int64_t in, int64_t* bytes) {
+    if (!bytes) return AQLM_ERR_NULL;
+    if (!generic_scheme_ok(M, B, g)) return AQLM_ERR_SCHEME;
+    if (out < 0 || out > (int64_t)INT32_MAX - 16 || in < 1 || in > AQLM_MAX_IN || (in % g) != 0)
+        return AQLM_ERR_SHAPE;
+    *bytes = (int64_t)packed_code_words(M, B, g, out, in) * 4;
+    return AQLM_OK;
+}
+
+int aqlm_pack_codes(const void* codes, void* packed, int M, int B, int g, int64_t out, int64_t in, void* stream) {
+    if (!generic_scheme_ok(M, B, g)) return AQLM_ERR_SCHEME;
+    if (out < 0 || out > (int64_t)INT32_MAX - 16 || in < 1 || in > AQLM_MAX_IN || (in % g) != 0)
+        return AQLM_ERR_SHAPE;
+    if (out == 0) return AQLM_OK;
+    if (!codes || !packed) return AQLM_ERR_NULL;
+    if (!aligned(codes, B <= 8 ? 1 : 2) || !aligned(packed, 4)) return AQLM_ERR_ALIGN;
+    return finish(launch_pack_codes(codes, packed, M, B, g, out, in, (hipStream_t)stream));
+}
+
+static int packed_call(Op op, const void* codes, const void* codebooks, const void* scales, const void* x, void* y,
+                       int M, int B, int g, int64_t out, int64_t in, int64_t batch, void* stream) {
+    int scheme = 0;
+    bool empty = false;
+    const int st = validate(op, codes, codebooks, scales, x, y, M, B, g, out, in, batch, &scheme, &empty, 4);
+    if (st != AQLM_OK || empty) return st;
+    GenericScheme sc{M, B, g};
+    sc.packed = true;
+    const hipStream_t s = (hipStream_t)stream;
+    if (op == Op::kGemv) return finish(launch_gemv_generic(sc, codes, codebooks, scales, x, y, out, in, batch, s));
+    if (op == Op::kGemm) return finish(launch_gemm_generic(sc, codes, codebooks, scales, x, y, out, in, batch, s));
+    return finish(launch_decode_generic(sc, codes, codebooks, scales, y, out, in, s));
+}
+
+int aqlm_linear_gemv_packed(const void* codes, const void* codebooks, const void* scales, const void* x, void* y,
+                            int M, int B, int g, int64_t out, int64_t in, int64_t batch, void* stream) {
+    return packed_call(Op::kGemv, codes, codebooks, scales, x, y, M, B, g, out, in, batch, stream);
+}
+
+int aqlm_linear_gemm_packed(const void* codes, const void* codebooks, const void* scales, const void* x, void* y,
+                            int M, int B, int g, int64_t out, int64_t in, int64_t batch, void* stream) {
+    return packed_call(Op::kGemm, codes, codebooks, scales, x, y, M, B, g, out, in, batch, stream);
+}
+
+int aqlm_linear_decode_packed(const void* codes, const void* codebooks, const void* scales, const void* x, void* y,
+                              int M, int B, int g, int64_t out, int64_t in, int64_t batch, void* stream) {
+    (void)batch;
+    return packed_call(Op::kDecode, codes, codebooks, scales, x, y, M, B, g, out, in, 1, stream);
 }
 
 int aqlm_gemm_dequant_workspace_bytes(int M, int B, int g, int64_t out, int64_t in, int64_t* bytes) {

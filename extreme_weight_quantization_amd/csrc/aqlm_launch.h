@@ -10,9 +10,17 @@ int device_cu_count();
 
 // A scheme other than 1x16 and 2x8 at g = 8: 1 <= M <= 8, 1 <= B <= 16,
 // g in {1, 2, 4, 8, 16, 32}; codes are uint8 for B <= 8, else 16-bit.
+// packed: the codes are one bit stream (code n in bits [n B, n B + B) of little-endian
+// 32-bit words, least significant bit first) instead of whole bytes per code.
 struct GenericScheme {
     int M, B, g;
+    bool packed = false;
 };
+// 32-bit words of the bit-packed codes of a layer, and the packing kernel (from the
+// whole-byte codes [out][in/g][M]).
+uint64_t packed_code_words(int M, int B, int g, int64_t out, int64_t in);
+hipError_t launch_pack_codes(const void* codes, void* words, int M, int B, int g, int64_t out, int64_t in,
+                             hipStream_t stream);
 
 hipError_t launch_decode_generic(const GenericScheme& sc, const void* codes, const void* codebooks,
                                  const void* scales, void* w, int64_t out, int64_t in, hipStream_t stream);

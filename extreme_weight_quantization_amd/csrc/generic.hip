@@ -38,11 +38,25 @@ constexpr size_t kGemmLdsCodebook = 65536;    // GEMM (next to its 40 KB of tile
 constexpr int kGemvMaxBatchGeneric = 16;
 constexpr int kGemvGenericThreads = 1024;     // 16 waves, one row each
 
-// The codeword index of code i: the low B bits of its CB-byte stored pattern.
+// The codeword index of code i: the low B bits of its CB-byte stored pattern, or,
+// for bit-packed codes (CB = 0), the B bits at bit i * B of the little-endian
+// 32-bit word stream (least significant bit first; a code may straddle two words,
+// and the second word is read only then).
 template <int CB>
-__device__ __forceinline__ uint32_t code_at(const uint8_t* __restrict__ codes, size_t i, uint32_t mask) {
-    if constexpr (CB == 1) return (uint32_t)codes[i] & mask;
-    else return (uint32_t)reinterpret_cast<const uint16_t*>(codes)[i] & mask;
+__device__ __forceinline__ uint32_t code_at(const uint8_t* __restrict__ codes, size_t i, uint32_t mask, int B) {
+    if constexpr (CB == 1) {
+        return (uint32_t)codes[i] & mask;
+    } else if constexpr (CB == 2) {
+        return (uint32_t)reinterpret_cast<const uint16_t*>(codes)[i] & mask;
+    } else {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(codes);
+        const uint64_t bit = (uint64_t)i * (uint64_t)B;
+        const size_t wi = (size_t)(bit >> 5);
+        const int off = (int)(bit & 31);
+        uint32_t v = w[wi] >> off;
+        if (off + B > 32) v |= w[wi + 1] << (32 - off);
+        return v & mask;
+    }
 }
 
 // N consecutive fp16 values starting at p (p aligned to 2N bytes, N <= 8).
@@ -72,10 +86,10 @@ __device__ __forceinline__ void load_f16(const f16* p, float (&v)[N]) {
 template <int G, int N, int CB>
 __device__ __forceinline__ void sum_codewords(const uint8_t* __restrict__ codes, size_t c0, const f16* cb,
                                               int M, int B, uint32_t mask, int t0, float (&v)[N]) {
-    load_f16<N>(cb + (size_t)code_at<CB>(codes, c0, mask) * G + t0, v);
+    load_f16<N>(cb + (size_t)code_at<CB>(codes, c0, mask, B) * G + t0, v);
     for (int m = 1; m < M; ++m) {
         float c[N];
-        load_f16<N>(cb + (((size_t)m << B) + code_at<CB>(codes, c0 + m, mask)) * G + t0, c);
+        load_f16<N>(cb + (((size_t)m << B) + code_at<CB>(codes, c0 + m, mask, B)) * G + t0, c);
 #pragma unroll
         for (int t = 0; t < N; ++t) v[t] = __fadd_rn(v[t], c[t]);
     }
@@ -454,19 +468,65 @@ hipError_t gemm_g(const GenericScheme& sc, const void* codes, const void* codebo
     return hipGetLastError();
 }
 
-// Returns CALL(G, CB) for the scheme's g and code width (1 byte for B <= 8, else 2).
+// Returns CALL(G, CB) for the scheme's g and code storage (CB = 1 byte for B <= 8,
+// 2 bytes for B <= 16, 0 for bit-packed codes).
+#define AQLM_CB(sc, G, CALL) (sc.packed ? CALL(G, 0) : (sc.B <= 8) ? CALL(G, 1) : CALL(G, 2))
 #define AQLM_DISPATCH_G(sc, CALL)                                       \
     switch (sc.g) {                                                     \
-        case 1: return (sc.B <= 8) ? CALL(1, 1) : CALL(1, 2);           \
-        case 2: return (sc.B <= 8) ? CALL(2, 1) : CALL(2, 2);           \
-        case 4: return (sc.B <= 8) ? CALL(4, 1) : CALL(4, 2);           \
-        case 8: return (sc.B <= 8) ? CALL(8, 1) : CALL(8, 2);           \
-        case 16: return (sc.B <= 8) ? CALL(16, 1) : CALL(16, 2);        \
-        case 32: return (sc.B <= 8) ? CALL(32, 1) : CALL(32, 2);        \
+        case 1: return AQLM_CB(sc, 1, CALL);                            \
+        case 2: return AQLM_CB(sc, 2, CALL);                            \
+        case 4: return AQLM_CB(sc, 4, CALL);                            \
+        case 8: return AQLM_CB(sc, 8, CALL);                            \
+        case 16: return AQLM_CB(sc, 16, CALL);                          \
+        case 32: return AQLM_CB(sc, 32, CALL);                          \
         default: return hipErrorInvalidValue;                           \
     }
 
+// Bit-packed codes from whole-byte ones: thread w builds 32-bit word w of the stream
+// from the (at most 33) codes that overlap its bits [32 w, 32 w + 32).
+template <int CB>
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restrict__ codes,
+                                                         uint32_t* __restrict__ words, uint64_t n_codes,
+                                                         uint64_t n_words, int B) {
+    const uint32_t mask = (1u << B) - 1u;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t w = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; w < n_words; w += stride) {
+        const uint64_t b0 = w * 32;
+        const uint64_t n0 = b0 / (uint64_t)B;
+        const uint64_t n1 = min(n_codes, (b0 + 32 + (uint64_t)B - 1) / (uint64_t)B);
+        uint32_t acc = 0u;
+        for (uint64_t n = n0; n < n1; ++n) {
+            const uint32_t v = code_at<CB>(codes, (size_t)n, mask, B);
+            const int64_t sh = (int64_t)(n * (uint64_t)B) - (int64_t)b0;   // -B < sh < 32
+            acc |= sh < 0 ? v >> (int)(-sh) : v << (int)sh;
+        }
+        words[w] = acc;
+    }
+}
+
 }  // namespace
+
+uint64_t packed_code_words(int M, int B, int g, int64_t out, int64_t in) {
+    const uint64_t n = (uint64_t)out * (uint64_t)(in / g) * (uint64_t)M;
+    return (n * (uint64_t)B + 31) / 32;
+}
+
+hipError_t launch_pack_codes(const void* codes, void* words, int M, int B, int g, int64_t out, int64_t in,
+                             hipStream_t stream) {
+    const uint64_t n_codes = (uint64_t)out * (uint64_t)(in / g) * (uint64_t)M;
+    const uint64_t n_words = packed_code_words(M, B, g, out, in);
+    if (n_words == 0) return hipSuccess;
+    uint64_t blocks = (n_words + 255) / 256;
+    const uint64_t cap = (uint64_t)device_cu_count() * 16;
+    if (blocks > cap) blocks = cap;
+    if (B <= 8)
+        hipLaunchKernelGGL(pack_codes_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const uint8_t*)codes, (uint32_t*)words, n_codes, n_words, B);
+    else
+        hipLaunchKernelGGL(pack_codes_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const uint8_t*)codes, (uint32_t*)words, n_codes, n_words, B);
+    return hipGetLastError();
+}
 
 hipError_t launch_decode_generic(const GenericScheme& sc, const void* codes, const void* codebooks,
                                  const void* scales, void* w, int64_t out, int64_t in, hipStream_t stream) {

@@ -157,6 +157,34 @@ int aqlm_linear_decode(const void* codes, const void* codebooks, const void* sca
                        int64_t out, int64_t in, int64_t batch, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Bit-packed codes ("Key AQLM quantization parameters" on the same page: a B
+ * that is not a multiple of 8 leaves unused bits in the bytes that hold each
+ * code; packing drops them, so e.g. (1, 12, 4) stores 3 bits per weight in its
+ * codes instead of 4).  Packed layout: the codes in their stored order
+ * ([out][in/g][M] flattened, code n = (i * in/g + j) * M + m) form one bit
+ * stream, code n in bits [n B, n B + B), least significant bit first; bit b is
+ * bit b % 32 of 32-bit word b / 32 (little-endian words); the stream is padded
+ * with zero bits to a whole word.  Rows are not padded (a row may start inside
+ * a word).  The buffer holds aqlm_packed_codes_bytes bytes and is 4-byte
+ * aligned.
+ *
+ * aqlm_linear_{gemv,gemm,decode}_packed take such a stream as `codes` and
+ * otherwise the arguments, validation and results of aqlm_linear_{gemv,gemm,
+ * decode} (decode bit-exact; every scheme of AQLM_ERR_SCHEME's range runs the
+ * general kernels); a misaligned stream gives AQLM_ERR_ALIGN.  aqlm_pack_codes
+ * writes the stream of whole-byte codes [out][in/g][M] (the low B bits of each
+ * stored code; every word of the stream, padding bits zero).
+ */
+int aqlm_packed_codes_bytes(int M, int B, int g, int64_t out, int64_t in, int64_t* bytes);
+int aqlm_pack_codes(const void* codes, void* packed, int M, int B, int g, int64_t out, int64_t in, void* stream);
+int aqlm_linear_gemv_packed(const void* codes, const void* codebooks, const void* scales, const void* x, void* y,
+                            int M, int B, int g, int64_t out, int64_t in, int64_t batch, void* stream);
+int aqlm_linear_gemm_packed(const void* codes, const void* codebooks, const void* scales, const void* x, void* y,
+                            int M, int B, int g, int64_t out, int64_t in, int64_t batch, void* stream);
+int aqlm_linear_decode_packed(const void* codes, const void* codebooks, const void* scales, const void* x, void* y,
+                              int M, int B, int g, int64_t out, int64_t in, int64_t batch, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Building the representation ("The AQLM quantization procedure" on the same
  * page: per layer, the codes are learned first with fixed codebooks that a
  * residual k-means initialises).  The page's learning loss is lost and needs

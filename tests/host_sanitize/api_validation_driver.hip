@@ -66,6 +66,10 @@ hipError_t launch_lists_fill(const void*, int64_t, int64_t, const void*, void*, 
 }
 hipError_t launch_gemv_lists(const void*, const void*, int64_t, const void*, const void*, const void*, void*,
                              void*, int64_t, int64_t, hipStream_t) { return stub(); }
+uint64_t packed_code_words(int M, int B, int g, int64_t out, int64_t in) {
+    return ((uint64_t)out * (uint64_t)(in / g) * (uint64_t)M * (uint64_t)B + 31) / 32;
+}
+hipError_t launch_pack_codes(const void*, void*, int, int, int, int64_t, int64_t, hipStream_t) { return stub(); }
 hipError_t lists_scratch(void** ptr) {
     static float fake[16];
     *ptr = fake;
@@ -161,6 +165,22 @@ int main() {
         CHECK(aqlm_linear_gemv_fused(1, nullptr, one, one, o1, x, yo, 2, 8, 8, 256, 1, st), AQLM_ERR_NULL, 0);
         CHECK(aqlm_linear_gemv_fused(1, one, one, one, nullptr, x, yo, 2, 8, 8, 256, 1, st), AQLM_ERR_NULL, 0);
     }
+
+    // ---- bit-packed codes: 4-byte aligned streams
+    int64_t pb = 0;
+    CHECK(aqlm_packed_codes_bytes(1, 12, 4, 64, 512, &pb), AQLM_OK, 0);
+    if (pb != 64 * 128 * 12 / 8) { fprintf(stderr, "packed bytes %lld\n", (long long)pb); ++g_failures; }
+    CHECK(aqlm_packed_codes_bytes(1, 12, 4, I64_MAX, 512, &pb), AQLM_ERR_SHAPE, 0);
+    CHECK(aqlm_packed_codes_bytes(1, 17, 4, 64, 512, &pb), AQLM_ERR_SCHEME, 0);
+    CHECK(aqlm_pack_codes(c, y, 1, 12, 4, 64, 512, st), AQLM_OK, 1);
+    CHECK(aqlm_pack_codes(c, buf + 2, 1, 12, 4, 64, 512, st), AQLM_ERR_ALIGN, 0);
+    CHECK(aqlm_pack_codes(nullptr, y, 1, 12, 4, 64, 512, st), AQLM_ERR_NULL, 0);
+    CHECK(aqlm_linear_gemv_packed(buf + 4, cb, s, x, y, 3, 5, 8, 64, 512, 4, st), AQLM_OK, 1);
+    CHECK(aqlm_linear_gemv_packed(buf + 2, cb, s, x, y, 3, 5, 8, 64, 512, 4, st), AQLM_ERR_ALIGN, 0);
+    CHECK(aqlm_linear_gemm_packed(buf + 4, cb, s, x, y, 2, 12, 8, 64, 512, 300, st), AQLM_OK, 1);
+    CHECK(aqlm_linear_decode_packed(buf + 4, cb, s, nullptr, y, 2, 12, 8, 64, 512, 0, st), AQLM_OK, 1);
+    CHECK(aqlm_linear_decode_packed(buf + 4, cb, s, x, y, 2, 12, 8, 64, 512, 0, st), AQLM_ERR_NULL, 0);
+    CHECK(aqlm_linear_gemv_packed(buf + 4, cb, s, x, y, 3, 5, 8, I64_MIN, 512, 4, st), AQLM_ERR_SHAPE, 0);
 
     // ---- two-pass prefill
     int64_t nb = -1;
