@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libaqlm.so")
 OBJ_DIR = os.path.join(os.path.dirname(PKG_DIR), "_build")
 SOURCES = ["aqlm_api.hip", "decode.hip", "gemv.hip", "gemm.hip", "gemm_pipe.hip", "generic.hip", "encode.hip",
-           "gemv_lists.hip", "gemm_dense.hip"]
+           "gemv_lists.hip", "gemm_dense.hip", "gemv_stream.hip"]
 ARCH = "gfx950"
 
 # No fast-math and no flush-to-zero: decode must be bit-exact.  Packed fp32

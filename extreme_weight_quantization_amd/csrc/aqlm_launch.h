@@ -65,6 +65,12 @@ hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, con
                        const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                        hipStream_t stream);
 
+// The streaming 2x8 product for batch 1-2 (gemv_stream.hip).  gemv_stream_lds: its LDS
+// bytes for layers whose workgroups are dealt, or 0 where it does not serve them.
+size_t gemv_stream_lds(const GemvLayers& layers, int64_t in, int64_t batch);
+hipError_t launch_gemv_stream(const GemvLayers& layers, const void* x, int64_t in, int64_t batch, size_t lds,
+                              hipStream_t stream);
+
 // 2x8 prefill product with the role-split pipeline; requires in % 64 == 0.
 hipError_t launch_gemm_pipe_2x8(const void* codes, const void* codebooks, const void* scales,
                                 const void* x, void* y, int64_t out, int64_t in, int64_t batch,

@@ -27,11 +27,15 @@
 //    looks up one cache line per lane, which made x the largest cost);
 //  * the 2x8 codebooks live in LDS, replicated REPL times with entry k of
 //    replica r at 16-byte slot (2k + m) * REPL + r; lane l reads replica
-//    l % REPL, which spreads the lanes served together over distinct bank
-//    groups.  REPL = 8 (64 KB, measured faster than 16: the smaller copy into
-//    LDS outweighs the extra conflicts) up to batch 8; with the 16-row x
-//    stage (128 KB) above batch 8 only 4 replicas fit.  1x16 codewords are
-//    gathered from the L2-resident 1 MiB codebook;
+//    l % REPL.  The LDS serves a 16-byte read to 16 lanes per clock from 16
+//    bank groups (measured: about 4.8 clocks a conflict-free wave read,
+//    8.5 when pairs of lanes share a group), so with REPL = 8 (64 KB, up to
+//    batch 8) lane l reads codebook (l / 8) % 2 first: the 16 lanes served
+//    together then touch 16 distinct groups.  With the 16-row x stage (128 KB)
+//    above batch 8 only 4 replicas fit.  1x16 codewords are gathered from the
+//    L2-resident 1 MiB codebook;
+//  * at batch 1-2 on layers with at least about five slab steps per wave the
+//    streaming kernel of gemv_stream.hip runs instead (gemv_stream_lds);
 //  * the other 2-bit schemes with B = 8 ("Key AQLM quantization parameters":
 //    1x8 g4, 4x8 g16, 8x8 g32 cost the same bits as 2x8) store in/4 code bytes
 //    per row too, so the same decomposition serves them; only the decode of a
@@ -128,11 +132,14 @@ __device__ __forceinline__ uint32_t code_byte(const u32x4 cv, int b) { return (c
 //   4x8 g16 / 8x8 g32: piece q is part q % H of group q / H (H = 2 or 4), the
 //     M codewords' parts added in fp32 from codebook 0 upward, rounded once
 //     (one piece at a time for 8x8, which would otherwise run out of registers).
-template <int SCHEME, int REPL>
+// MASKED false: every piece of the chunk is inside the matrix (a whole slab of a
+// whole row tile), and ok_mask is not read.
+template <int SCHEME, int REPL, bool MASKED>
 __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restrict__ cb_lds,
                                             const f16* __restrict__ codebooks, int rrep,
                                             uint32_t ok_mask, const f16x8 (&bx)[8], f32x4 acc) {
     constexpr int M = b8_codebooks(SCHEME);
+    auto keep = [&](int p) { return !MASKED || ((ok_mask >> p) & 1); };
     if constexpr (M == 1) {
         const u32x2* cb8 = reinterpret_cast<const u32x2*>(cb_lds);
 #pragma unroll
@@ -147,7 +154,7 @@ __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restr
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                a[q] = ((ok_mask >> (4 * h + q)) & 1) ? a[q] : f16x8{};
+                a[q] = keep(4 * h + q) ? a[q] : f16x8{};
                 acc = mfma16x16x32(a[q], bx[4 * h + q], acc);
             }
         }
@@ -168,7 +175,7 @@ __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restr
             f16x8 a;
 #pragma unroll
             for (int t = 0; t < 8; ++t) a[t] = (f16)sum[t];
-            a = ((ok_mask >> q) & 1) ? a : f16x8{};
+            a = keep(q) ? a : f16x8{};
             acc = mfma16x16x32(a, bx[q], acc);
             if constexpr (M == 8) __builtin_amdgcn_sched_barrier(0);
         }
@@ -177,7 +184,29 @@ __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restr
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         f16x8 a[4];
-        if constexpr (SCHEME == kScheme2x8) {
+        if constexpr (SCHEME == kScheme2x8 && REPL == 8) {
+            // The two reads of a group take the codebooks in the order (mA, 1 - mA) with
+            // mA = (lane / 8) % 2, so the 16 lanes served together read 16 distinct 16-byte
+            // bank groups of a 256-byte LDS row (codeword k of codebook m, replica r at byte
+            // 256 k + 128 m + 16 r).  v_perm_b32 assembles an address in one instruction:
+            // byte 0 from base (16 r + 128 m), byte 1 the code byte, bytes 2-3 zero.  The
+            // fp16 sum of the two codewords does not depend on the order of its operands.
+            const uint32_t lane = threadIdx.x & (kWave - 1);
+            const uint32_t mA = (lane >> 3) & 1u, r16 = (lane & 7u) * 16u;
+            const uint32_t base = (r16 + 128u * mA) | ((r16 + 128u * (mA ^ 1u)) << 8);
+            const char* cbb = reinterpret_cast<const char*>(cb_lds);
+            f16x8 c1[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t d = cv[2 * h + (q >> 1)], hw = 2u * (q & 1);
+                const uint32_t ra = __builtin_amdgcn_perm(base, d, 0x0c0c0004u | ((hw + mA) << 8));
+                const uint32_t rb = __builtin_amdgcn_perm(base, d, 0x0c0c0005u | ((hw + (mA ^ 1u)) << 8));
+                a[q] = as_f16x8(*reinterpret_cast<const u32x4*>(cbb + ra));
+                c1[q] = as_f16x8(*reinterpret_cast<const u32x4*>(cbb + rb));
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[q] = keep(4 * h + q) ? a[q] + c1[q] : f16x8{};
+        } else if constexpr (SCHEME == kScheme2x8) {
             f16x8 c1[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -186,7 +215,7 @@ __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restr
                 c1[q] = as_f16x8(cb_lds[(2 * (c >> 8) + 1) * REPL + rrep]);
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) a[q] = ((ok_mask >> (4 * h + q)) & 1) ? a[q] + c1[q] : f16x8{};
+            for (int q = 0; q < 4; ++q) a[q] = keep(4 * h + q) ? a[q] + c1[q] : f16x8{};
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -194,7 +223,7 @@ __device__ __forceinline__ f32x4 chunk_mfma(const u32x4 cv, const u32x4* __restr
                 a[q] = as_f16x8(load16(codebooks + (size_t)c * kGroup));
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) a[q] = ((ok_mask >> (4 * h + q)) & 1) ? a[q] : f16x8{};
+            for (int q = 0; q < 4; ++q) a[q] = keep(4 * h + q) ? a[q] : f16x8{};
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc = mfma16x16x32(a[q], bx[4 * h + q], acc);
@@ -220,7 +249,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int G = in / kGroup;
     const int n_slab = (G + kSlabGroups - 1) / kSlabGroups;
     const int n_rt = (out + kRowTile - 1) / kRowTile;
@@ -384,12 +413,17 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
 #pragma unroll
             for (int q = 0; q < 8; ++q)
                 gmask |= (s * kSlabGroups + slab_group(kq, q) < G) ? (1u << q) : 0u;
+            const bool whole_slab = (s + 1) * kSlabGroups <= G;   // uniform over the wave
 #pragma unroll
             for (int i = 0; i < RTP; ++i) {
                 const int rt = rt0 + i * nwg;
                 if (rt >= n_rt) break;
-                const uint32_t ok = (rt * kRowTile + lrow < out) ? gmask : 0u;
-                acc[i] = chunk_mfma<SCHEME, REPL>(ccur[i], smem, codebooks, rrep, ok, bx, acc[i]);
+                if (whole_slab && (rt + 1) * kRowTile <= out) {
+                    acc[i] = chunk_mfma<SCHEME, REPL, false>(ccur[i], smem, codebooks, rrep, 0u, bx, acc[i]);
+                } else {
+                    const uint32_t ok = (rt * kRowTile + lrow < out) ? gmask : 0u;
+                    acc[i] = chunk_mfma<SCHEME, REPL, true>(ccur[i], smem, codebooks, rrep, ok, bx, acc[i]);
+                }
             }
         }
 
@@ -562,7 +596,11 @@ hipError_t launch_gemv_fused(int scheme, GemvLayers layers, const void* x, int64
     if (layers.n < 1) return hipSuccess;
     deal_workgroups(layers, device_cu_count());
     const int n = (int)in, T = (int)batch;
-    if (scheme == kScheme2x8) return launch_gemv_2x8<RTP>(layers, x, n, T, stream);
+    if (scheme == kScheme2x8) {
+        const size_t lds = gemv_stream_lds(layers, in, batch);
+        if (lds > 0) return launch_gemv_stream(layers, x, in, batch, lds, stream);
+        return launch_gemv_2x8<RTP>(layers, x, n, T, stream);
+    }
     if (scheme == kScheme1x16) return launch_gemv_1x16<RTP>(layers, x, n, T, stream);
     return launch_gemv_b8<RTP>(scheme, layers, x, n, T, stream);
 }

@@ -160,6 +160,24 @@ def test_gemv_small(scheme, out, n_in, batch):
     assert_close(y, y_ref, f"{scheme} {out}x{n_in} b{batch}")
 
 
+@pytest.mark.parametrize("out,n_in,batch", [
+    (33, 4160, 1),      # 16 whole slabs and a ragged one, ragged row tile
+    (33, 4160, 2),
+    (4104, 256, 2),     # one slab: 16 waves split the row tiles, no slab parts
+    (4104, 320, 1),     # a ragged second slab is all that one slab part holds
+    (100, 192, 1),      # no whole slab at all
+    (20000, 512, 1),    # several row tiles per wave in turn
+    (70000, 256, 2),    # 18 row tiles per workgroup
+    (64, 28672, 2),     # long slab ranges: 7 slabs a wave
+])
+def test_gemv_2x8_batch_1_2_every_output(out, n_in, batch):
+    """The 2x8 product at batch 1-2 over 64-aligned inputs (codes and x streamed, the
+    ragged last slab handled apart from the whole ones), every output against the oracle."""
+    L = synth.make_layer("2x8", out, n_in, batch=batch, seed=out + n_in)
+    y = run_gemv(L)
+    assert_close_all(y, ref_full(L), f"2x8 {out}x{n_in} b{batch}")
+
+
 @pytest.mark.parametrize("scheme", ["2x8", "1x16"])
 @pytest.mark.parametrize("batch", [3, 16])
 def test_gemv_several_passes_and_slabs(scheme, batch):
@@ -271,6 +289,8 @@ def run_fused(layers, x):
     ((4096,) * 4, 11008, 16),             # 64 workgroups a layer: two passes of three slabs a wave
     ((11008, 11008), 4096, 4),            # gate, up of a 7B MLP
     ((100, 4096, 37, 1000), 520, 3),      # ragged rows and in, uneven layers
+    ((100, 4096, 37, 1000), 576, 1),      # ragged rows and last slab, 64-aligned in
+    ((28672, 28672), 8192, 2),            # 70B gate, up: 14 row tiles per workgroup
     ((16,) * 8, 256, 1),                  # the most layers one call takes
 ])
 def test_gemv_fused_matches_separate_and_oracle(scheme, outs, n_in, batch):
