@@ -16,7 +16,8 @@ Also measured in the same run (reported under "breakdown", not in value): the
 same block with the codes in their stored layout (aqlm_linear_gemv, per-code
 codebook gathers), alone and with q,k,v and gate,up fused; 2x8 GEMV at batch
 1/4/16 on the same block; the Llama-2-70B 1x16 layers at batch 1 in both
-layouts; the 2048-token prefill GEMM on the 7B shapes (both schemes); the
+layouts; the 70B layers as 2x8 at batch 1, alone, in aggregate and as a block
+step with q,k,v and gate,up fused; the 2048-token prefill GEMM on the 7B shapes (both schemes); the
 standalone decode kernel; the other 2-bit schemes; the encoder; and the fp16
 comparator.  Secondary figures: the headline as a share of a measured
 device-to-device copy's bandwidth, the effective weight rate (fp16-equivalent
@@ -50,6 +51,8 @@ LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 BLOCK_7B = ((4096, 4096),) * 4 + ((11008, 4096),) * 2 + ((4096, 11008),)
 SHAPES_7B = ((4096, 4096), (11008, 4096), (4096, 11008))
 SHAPES_70B = ((8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672))
+# A Llama-2-70B decoder block in the same order as BLOCK_7B: q, k, v (GQA), o, gate, up, down.
+BLOCK_70B = ((8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192), (28672, 8192), (8192, 28672))
 SCHEMES = {"2x8": (2, 8, 8, 0.05), "1x16": (1, 16, 8, 0.02)}
 
 
@@ -492,7 +495,38 @@ def main():
                 "stored_layout_GBps": round(ls3.bytes_per_step / (k3p * 1e-6) / 1e9, 1)}
             del ls3
             torch.cuda.empty_cache()
+        t70 = sum(v["us"] for v in r70.values())
+        b70 = sum(gemv_bytes(o, i, 1) for o, i in SHAPES_70B)
+        r70["aggregate"] = {"what": "sum of bytes over sum of per-layer times, the four 70B shapes once each",
+                            "us": round(t70, 3), "GBps": round(b70 / (t70 * 1e-6) / 1e9, 1),
+                            "pct_hbm_peak": round(100 * b70 / (t70 * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
         breakdown["gemv_1x16_b1_70b"] = r70
+        # 70B layers, 2x8, batch 1: each shape alone, their aggregate, and a 70B block
+        # step with q,k,v and gate,up fused (the streaming kernel's large layers)
+        r70b = {}
+        for shape in SHAPES_70B:
+            ls4 = LayerSet(torch, "2x8", (shape,), 1, sets_needed((shape,), 1, cap=16), seed=4)
+            _, sh4 = time_gemv(torch, E, ls4, iters, 5)
+            k4 = sh4[shape]
+            r70b[f"{shape[0]}x{shape[1]}"] = {
+                "us": round(k4, 3), "GBps": round(ls4.bytes_per_step / (k4 * 1e-6) / 1e9, 1),
+                "pct_hbm_peak": round(100 * ls4.bytes_per_step / (k4 * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+            del ls4
+            torch.cuda.empty_cache()
+        t70b = sum(v["us"] for v in r70b.values())
+        r70b["aggregate"] = {"what": "sum of bytes over sum of per-layer times, the four 70B shapes once each",
+                             "us": round(t70b, 3), "GBps": round(b70 / (t70b * 1e-6) / 1e9, 1),
+                             "pct_hbm_peak": round(100 * b70 / (t70b * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        ls5 = LayerSet(torch, "2x8", BLOCK_70B, 1, sets_needed(BLOCK_70B, 1, cap=8), seed=5)
+        spot_check(torch, E, ls5)
+        ms5 = time_fused_block(torch, E, ls5, max(10, iters // 2), 3)
+        r70b["block_fused"] = {"what": "one 70B block per step: q,k,v fused | o | gate,up fused | down",
+                               "ms_per_step": round(ms5, 5),
+                               "GBps_step": round(ls5.bytes_per_step / (ms5 * 1e-3) / 1e9, 1),
+                               "pct_hbm_peak": round(100 * ls5.bytes_per_step / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        del ls5
+        torch.cuda.empty_cache()
+        breakdown["gemv_2x8_b1_70b"] = r70b
         breakdown["gemv_fused_7b_block"] = fused
         # prefill GEMM, 2048 tokens
         gen = torch.Generator(device="cuda")
@@ -650,6 +684,9 @@ def main():
             "codes_layout": "slice lists (aqlm_lists_pack once per layer at load, outside the timed region; "
                             "the stored layout's figures are under breakdown)",
             "entry_bytes_per_step": int(entry_bytes_step),
+            "served_bits_per_weight": round(8.0 * entry_bytes_step / sum(o * i for o, i in BLOCK_7B), 3),
+            "stored_layout_GBps": (None if args.quick else
+                                   breakdown["gemv_1x16_b1_7b_stored_layout"]["GBps_step"]),
             "rotated_buffer_sets": n_sets, "parallelism": "single GPU",
             "us_per_layer": round(ms_step * 1e3 / len(BLOCK_7B), 3),
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
