@@ -156,6 +156,8 @@ int aqlm_linear_gemm(const void* codes, const void* codebooks, const void* scale
     if (st != AQLM_OK || empty) return st;
     if (M == 1 && B == 8 && g == 4 && in % 64 == 0)   // the 2x8 pipeline with two 4-entry codewords a piece
         return finish(launch_gemm_pipe_1x8g4(codes, codebooks, scales, x, y, out, in, batch, (hipStream_t)stream));
+    if (M == 4 && B == 8 && g == 16 && in % 64 == 0)   // the 2x8 pipeline, four 16-entry codewords a group
+        return finish(launch_gemm_pipe_4x8g16(codes, codebooks, scales, x, y, out, in, batch, (hipStream_t)stream));
     if (scheme == kSchemeGeneric)
         return finish(launch_gemm_generic(GenericScheme{M, B, g}, codes, codebooks, scales, x, y, out, in,
                                           batch, (hipStream_t)stream));

@@ -1,8 +1,10 @@
 // Prefill product for the 2x8 scheme with a role-split software pipeline:
 //   Y[t][i] = s[i] * sum_k X[t][k] Wc[i][k],  Wc[i][8j+u] = C0[b0][u] + C1[b1][u].
-// The same kernel serves 1x8 g4, whose codes also take 2 bytes per 8 inputs at
-// the same places: there the 8 weights of a piece are two 4-entry codewords,
-// Wc[i][8j+u] = C0[b_{2j}][u] for u < 4 and C0[b_{2j+1}][u-4] above.
+// The same kernel serves the other 2-bit schemes whose codes also take 2 bytes
+// per 8 inputs at the same places ("Key AQLM quantization parameters"): 1x8 g4,
+// where the 8 weights of a piece are two 4-entry codewords, Wc[i][8j+u] =
+// C0[b_{2j}][u] for u < 4 and C0[b_{2j+1}][u-4] above, and 4x8 g16, where a
+// group of 16 inputs is the sum of four 16-entry codewords (4 code bytes).
 //
 // "The AQLM Quantization Algorithm, Explained", Figure 2 of the MCQ section:
 // the product runs on dequantized half-precision weights, each built from one
@@ -36,8 +38,9 @@
 //                     B_k waits for the codes of step k+2.
 // X tiles thus have two steps to arrive, code loads about kRing-2.  X keeps
 // three stages, W two (a W tile is written one step before it is read), the
-// code ring kRing steps: 96 + 32 + 24 + 8 (codebooks; 2 KB for 1x8 g4) = 160 KB.  The products
-// run in the order of a plain k loop.
+// code ring kRing steps: 96 + 32 + 24 + 8 (codebooks; 2 KB for 1x8 g4) = 160 KB.  4x8 g16
+// keeps two X stages next to its 32 KB of codebooks (64 + 32 + 24 + 32 = 152 KB), so its X
+// tiles have one step to arrive.  The products run in the order of a plain k loop.
 //
 // Epilogue (out % 8 == 0): producers and consumers meet at a last barrier; then
 // each consumer wave passes its scaled 64x64 tile through LDS and stores whole
@@ -69,16 +72,25 @@ constexpr int kPipeRing = 12;                // steps of codes held in LDS
 // codebook slots: 2x8 codeword k of codebook m at 256 m + k (the codebooks one after the
 // other: a producer read of one codebook then spreads its lanes over all 16 bank groups,
 // where interleaved codebooks left it 8; 4096^2 at 2048 tokens 80.4 -> 74.9 us); 1x8 g4
-// codeword k in 8-byte slot k
+// codeword k in 8-byte slot k; 4x8 g16 half h (8 entries) of codeword k of codebook m at
+// 1024 h + 256 m + k (32 KB).
 template <int SCHEME>
-constexpr int pipe_cb_slots() { return SCHEME == kScheme2x8 ? 2 * kCodewords2x8 : kCodewords2x8 / 2; }
-constexpr int kPipeCb = pipe_cb_slots<kScheme2x8>();   // the larger of the two
-constexpr int kPipeXOff = 0;
-constexpr int kPipeWOff = kPipeXOff + 3 * kPipeXStage;
-constexpr int kPipeRingOff = kPipeWOff + kPipeWStages * kPipeWStage;
-constexpr int kPipeCbOff = kPipeRingOff + kPipeRing * kPipeBN;
-constexpr size_t kPipeLds = (size_t)(kPipeCbOff + kPipeCb) * 16;
-static_assert(kPipeLds <= 163840, "LDS budget");
+constexpr int pipe_cb_slots() {
+    return SCHEME == kScheme2x8 ? 2 * kCodewords2x8 : SCHEME == kSchemeB8M4 ? 8 * kCodewords2x8 : kCodewords2x8 / 2;
+}
+// X stages: three (X loads get two steps to land), or two for 4x8 g16, whose 32 KB of
+// codebooks leave no room for a third (its X loads get one step).
+template <int SCHEME>
+constexpr int pipe_x_stages() { return SCHEME == kSchemeB8M4 ? 2 : 3; }
+template <int SCHEME>
+struct PipeLayout {   // offsets in 16-byte slots
+    static constexpr int kX = 0;
+    static constexpr int kW = kX + pipe_x_stages<SCHEME>() * kPipeXStage;
+    static constexpr int kRing = kW + kPipeWStages * kPipeWStage;
+    static constexpr int kCb = kRing + kPipeRing * kPipeBN;
+    static constexpr size_t kBytes = (size_t)(kCb + pipe_cb_slots<SCHEME>()) * 16;
+    static_assert(kBytes <= 163840, "LDS budget");
+};
 
 __device__ __forceinline__ int stage_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
 
@@ -88,10 +100,12 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
     const f16* __restrict__ scales, const f16* __restrict__ x, f16* __restrict__ y,
     int out, int in, int T) {
     extern __shared__ u32x4 smem[];
-    u32x4* Xs = smem + kPipeXOff;       // [stage 3][kPipeXStage]
-    u32x4* Ws = smem + kPipeWOff;       // [stage 2][kPipeWStage]
-    u32x4* ring = smem + kPipeRingOff;  // [kPipeRing][row 128] : the 8 group codes of a row, 16 bytes
-    u32x4* cb = smem + kPipeCbOff;
+    using Lay = PipeLayout<SCHEME>;
+    constexpr int kXS = pipe_x_stages<SCHEME>();
+    u32x4* Xs = smem + Lay::kX;         // [stage kXS][kPipeXStage]
+    u32x4* Ws = smem + Lay::kW;         // [stage 2][kPipeWStage]
+    u32x4* ring = smem + Lay::kRing;    // [kPipeRing][row 128] : the codes of a row's 64 inputs, 16 bytes
+    u32x4* cb = smem + Lay::kCb;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = in / kGroup;
     const int n_k = G / 8;                          // the launcher guarantees in % 64 == 0
@@ -100,8 +114,12 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
     const int t0 = (int)(blockIdx.x % n_tt) * kPipeBM;
 
     if constexpr (SCHEME == kScheme2x8) {
-        for (int j = tid; j < kPipeCb; j += kPipeThreads)
+        for (int j = tid; j < pipe_cb_slots<SCHEME>(); j += kPipeThreads)
             cb[j] = load16(codebooks + (size_t)j * kGroup);
+    } else if constexpr (SCHEME == kSchemeB8M4) {
+        // slot j = 1024 h + km (km = 256 m + k): entries 8 h .. 8 h + 7 of codeword km
+        for (int j = tid; j < pipe_cb_slots<SCHEME>(); j += kPipeThreads)
+            cb[j] = load16(codebooks + (size_t)(j & 1023) * 16 + (j >> 10) * 8);
     } else {
         u32x2* cb8 = reinterpret_cast<u32x2*>(cb);
         for (int j = tid; j < kCodewords2x8; j += kPipeThreads)
@@ -143,6 +161,21 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) d[stage_slot(r, c0 + q)] = as_u32x4(e[2 * q] + e[2 * q + 1]);
+            } else if constexpr (SCHEME == kSchemeB8M4) {
+                // piece c0 + q (c0 even): half q % 2 of group c0 / 2 + q / 2 (16 inputs), whose
+                // 4 code bytes are dword c0 / 2 + q / 2 of the row's step; the four codewords'
+                // halves added in fp16 from codebook 0 up
+                f16x8 t[4][4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t cd = q < 2 ? ca : cw;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        t[q][m] = as_f16x8(cb[1024 * (q & 1) + 256 * m + ((cd >> (8 * m)) & 0xff)]);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    d[stage_slot(r, c0 + q)] = as_u32x4(((t[q][0] + t[q][1]) + t[q][2]) + t[q][3]);
             } else {
                 // piece c0 + q: groups 2 (c0 + q) and 2 (c0 + q) + 1, one byte each
                 const u32x2* cb8 = reinterpret_cast<const u32x2*>(cb);
@@ -187,11 +220,11 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
 
     // ------------------------------ consumers ------------------------------
     const int wm = wave >> 1, wn = wave & 1;
-    // X of step j into stage j % 3: load q writes slots 64q .. 64q+63, lane l the chunk
+    // X of step j into stage j % kXS: load q writes slots 64q .. 64q+63, lane l the chunk
     // (l % 8) ^ ((rr >> 1) & 7) of row rr = 8q + l/8 (8 whole 128-byte lines per load)
     auto load_x = [&](int j) {
         const int jc = min(j, n_k - 1);
-        u32x4* dst = Xs + (j % 3) * kPipeXStage;
+        u32x4* dst = Xs + (j % kXS) * kPipeXStage;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q = 4 * wave + i;
@@ -208,7 +241,7 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto read_frags = [&](int j, int h, f16x8 (&a)[4], f16x8 (&b)[4]) {
-        const u32x4* xb = Xs + (j % 3) * kPipeXStage;
+        const u32x4* xb = Xs + (j % kXS) * kPipeXStage;
         const u32x4* wb = Ws + (j % kPipeWStages) * kPipeWStage;
         const int c = 4 * h + (lane >> 4);
 #pragma unroll
@@ -229,11 +262,11 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
         }
     };
     load_x(0);
-    load_x(1);
+    if constexpr (kXS == 3) load_x(1);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // P1: codebook copy staged
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");     // P2: X(0), X(1) landed, W(0) written
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");     // P2: X(0) (and X(1)) landed, W(0) written
     f16x8 a0[4], b0[4], a1[4], b1[4];
-    load_x(2);
+    load_x(kXS - 1);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(0, 0, a0, b0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -241,10 +274,14 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
     mma16(a0, b0);
     for (int k = 1; k < n_k; ++k) {
         __builtin_amdgcn_sched_barrier(0);
-        // B_{k-1}: the four X loads of step k-1 stay in flight, all earlier ones have landed
-        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // B_{k-1}: X(k) has landed.  Three stages: the four X loads issued after it, those of
+        // step k+1, stay in flight; two stages: X(k) is the last load issued.
+        if constexpr (kXS == 3)
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        load_x(k + 2);          // stage (k-1) % 3: step k-1 was read before B_{k-1}
+        load_x(k + kXS - 1);    // stage (k-1) % kXS: step k-1 was read before B_{k-1}
         __builtin_amdgcn_sched_barrier(0);
         read_frags(k, 0, a0, b0);
         mma16(a1, b1);          // half 1 of step k-1
@@ -310,7 +347,7 @@ template <int SCHEME>
 static hipError_t launch_pipe(const void* codes, const void* codebooks, const void* scales, const void* x, void* y,
                               int64_t out, int64_t in, int64_t batch, hipStream_t stream) {
     if (in % 64 != 0) return hipErrorInvalidValue;
-    const size_t lds = kPipeLds - (size_t)(kPipeCb - pipe_cb_slots<SCHEME>()) * 16;
+    const size_t lds = PipeLayout<SCHEME>::kBytes;
     const hipError_t e = hipFuncSetAttribute((const void*)gemm_pipe_2x8_kernel<SCHEME>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -331,6 +368,12 @@ hipError_t launch_gemm_pipe_1x8g4(const void* codes, const void* codebooks, cons
                                   const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                                   hipStream_t stream) {
     return launch_pipe<kSchemeB8M1>(codes, codebooks, scales, x, y, out, in, batch, stream);
+}
+
+hipError_t launch_gemm_pipe_4x8g16(const void* codes, const void* codebooks, const void* scales,
+                                   const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                                   hipStream_t stream) {
+    return launch_pipe<kSchemeB8M4>(codes, codebooks, scales, x, y, out, in, batch, stream);
 }
 
 }  // namespace aqlm

@@ -522,6 +522,17 @@ def test_gemm_1x8g4_pipeline(out, n_in, batch):
                  f"1x8g4 gemm {out}x{n_in} T{batch}")
 
 
+@pytest.mark.parametrize("out,n_in,batch", [(300, 1088, 130), (129, 64, 257), (64, 2048, 1), (4104, 4096, 300)])
+def test_gemm_4x8g16_pipeline(out, n_in, batch):
+    """4x8 g16 with in % 64 == 0 runs the pipelined 2x8 prefill with two X stages: ragged rows
+    and tokens, a single k-step, a single token, many row tiles; every output."""
+    L = synth.make_layer_mbg(4, 8, 16, out, n_in, batch=batch, seed=out + 3 * batch)
+    c, cb, s, x = gdev(L, L.codes)
+    y = E.aqlm_linear_gemm(c, cb, s, x)
+    torch.cuda.synchronize()
+    assert_close_all(y.cpu().numpy(), ref_full(L), f"4x8g16 gemm {out}x{n_in} T{batch}")
+
+
 @pytest.mark.parametrize("M,B,g", [(4, 8, 16), (1, 8, 4), (3, 5, 2)])
 def test_generic_exact_on_identity(M, B, g):
     """Dyadic one-hot codebooks and X = I: GEMM and GEMV return W16 columns exactly."""
