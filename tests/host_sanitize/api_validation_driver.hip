@@ -51,6 +51,8 @@ hipError_t launch_gemm_pipe_2x8(const void*, const void*, const void*, const voi
                                 int64_t, hipStream_t) { return stub(); }
 hipError_t launch_gemm_pipe_1x8g4(const void*, const void*, const void*, const void*, void*, int64_t, int64_t,
                                   int64_t, hipStream_t) { return stub(); }
+hipError_t launch_gemm_pipe_4x8g16(const void*, const void*, const void*, const void*, void*, int64_t, int64_t,
+                                  int64_t, hipStream_t) { return stub(); }
 hipError_t launch_gemm_dense(const void*, const void*, void*, int64_t, int64_t, int64_t, hipStream_t) {
     return stub();
 }
