@@ -20,9 +20,14 @@
 //    takes a contiguous range of the slabs (min(16, slabs) ranges) and walks
 //    its tiles one after another, each over its whole range, so the two halves
 //    of a row's 128-byte line are read back to back by the same wave;
-//  * the codes of the next 4 steps are in flight in a ring of registers whose
+//  * the codes of the next 2 steps are in flight in a ring of registers whose
 //    slots are fixed at compile time, refilled unconditionally after their last
-//    use, so the compiler waits for the oldest load only;
+//    use, so the compiler waits for the oldest load only (two steps a wave, 2 KB,
+//    stream faster than three or four: with 16 waves a CU the deeper rings
+//    queue more requests than HBM serves well);
+//  * a step issues its 16 codebook reads before its first product, and the
+//    kernels are compiled for at most 4 waves a SIMD (one workgroup a CU), so
+//    the registers for all 16 codewords are there;
 //  * each wave writes one fp32 partial per (tile, row, batch column) to LDS at
 //    the end of its range of a tile; after the last tile one barrier, and the
 //    partials of a tile are added in slab-range order, scaled and rounded.  A
@@ -46,7 +51,7 @@ constexpr int kSThreads = kSWaves * kWave;
 constexpr int kSSlab = 32;                                  // groups per slab
 constexpr int kSRepl = 8;                                   // codebook replicas
 constexpr int kSCbBytes = 2 * kCodewords2x8 * kSRepl * 16;   // 64 KB
-constexpr int kSRing = 4;                                   // steps of codes in flight per wave
+constexpr int kSRing = 2;                                   // steps of codes in flight per wave
 constexpr int kSMaxT = 2;
 constexpr int kSMinSteps = 5;                               // slab steps per wave below which gemv_kernel serves
 
@@ -60,26 +65,28 @@ __device__ __forceinline__ u32x4 lds16(uint32_t byte) {
 // of its row in the slab, two codewords each) added to acc.  Codeword k of codebook m, replica r is
 // at LDS byte 256 k + 128 m + 16 r; lane l uses replica l % 8 and reads codebook
 // mA = (l / 8) % 2 first.  base: byte 0 = 16 r + 128 mA, byte 1 = 16 r + 128 (1 - mA).
-// MASKED: pieces whose ok bit is clear contribute zero.
+// All 16 reads are issued before the first product.  MASKED: pieces whose ok bit
+// is clear contribute zero.
 template <bool MASKED>
 __device__ __forceinline__ f32x4 chunk_2x8(const u32x4 cv, uint32_t base, uint32_t mA, uint32_t ok,
                                            const f16x8 (&bx)[8], f32x4 acc) {
+    f16x8 a[8], b[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        f16x8 a[4], b[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint32_t d = cv[2 * h + (q >> 1)], hw = 2u * (q & 1);
-            a[q] = as_f16x8(lds16(__builtin_amdgcn_perm(base, d, 0x0c0c0004u | ((hw + mA) << 8))));
-            b[q] = as_f16x8(lds16(__builtin_amdgcn_perm(base, d, 0x0c0c0005u | ((hw + (mA ^ 1u)) << 8))));
+            a[4 * h + q] = as_f16x8(lds16(__builtin_amdgcn_perm(base, d, 0x0c0c0004u | ((hw + mA) << 8))));
+            b[4 * h + q] = as_f16x8(lds16(__builtin_amdgcn_perm(base, d, 0x0c0c0005u | ((hw + (mA ^ 1u)) << 8))));
         }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            f16x8 w = a[q], w2 = b[q];
-            if constexpr (MASKED) { w = ((ok >> (4 * h + q)) & 1u) ? w : f16x8{}; w2 = ((ok >> (4 * h + q)) & 1u) ? w2 : f16x8{}; }
-            acc = mfma16x16x32(w, bx[4 * h + q], acc);
-            acc = mfma16x16x32(w2, bx[4 * h + q], acc);
-        }
+    for (int q = 0; q < 8; ++q) {
+        f16x8 w = a[q], w2 = b[q];
+        if constexpr (MASKED) { w = ((ok >> q) & 1u) ? w : f16x8{}; w2 = ((ok >> q) & 1u) ? w2 : f16x8{}; }
+        acc = mfma16x16x32(w, bx[q], acc);
+        acc = mfma16x16x32(w2, bx[q], acc);
     }
     return acc;
 }
@@ -236,7 +243,9 @@ __device__ __forceinline__ void stream_body(const uint8_t* __restrict__ codes, c
 }
 
 template <int D>
-__global__ __launch_bounds__(kSThreads) void gemv_stream_kernel(const uint8_t* __restrict__ codes,
+// One workgroup of 16 waves a CU (its LDS): at most 4 waves a SIMD, so the compiler
+// may use up to 128 registers a lane instead of packing for a higher occupancy.
+__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_stream_kernel(const uint8_t* __restrict__ codes,
                                                                 const f16* __restrict__ codebooks,
                                                                 const f16* __restrict__ scales, f16* __restrict__ y,
                                                                 int out, const f16* __restrict__ x, int in, int T) {
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(kSThreads) void gemv_stream_kernel(const uint8_t* _
 
 // Several layers that share x; the workgroup's layer is found as in gemv_fused_kernel.
 template <int D>
-__global__ __launch_bounds__(kSThreads) void gemv_stream_fused_kernel(const GemvLayers L, const f16* __restrict__ x,
+__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_stream_fused_kernel(const GemvLayers L, const f16* __restrict__ x,
                                                                       int in, int T) {
     int li = 0, wg0 = 0, wg1 = L.wg_end[0];
 #pragma unroll
