@@ -590,17 +590,71 @@ static hipError_t launch_gemv_1x16(const GemvLayers& layers, const void* x, int 
     return launch_gemv_v<kScheme1x16, 1, RTP, kXStaged16>(layers, x, n, T, stream);
 }
 
+// Layer l of a group as a group of its own.
+static GemvLayers one_layer(const GemvLayers& g, int l) {
+    GemvLayers one = {};
+    one.codes[0] = g.codes[l];
+    one.codebooks[0] = g.codebooks[l];
+    one.scales[0] = g.scales[l];
+    one.y[0] = g.y[l];
+    one.out[0] = g.out[l];
+    one.n = 1;
+    return one;
+}
+
+static void add_layer(GemvLayers& g, const GemvLayers& from, int l) {
+    g.codes[g.n] = from.codes[l];
+    g.codebooks[g.n] = from.codebooks[l];
+    g.scales[g.n] = from.scales[l];
+    g.y[g.n] = from.y[l];
+    g.out[g.n] = from.out[l];
+    ++g.n;
+}
+
+// 2x8: the streaming kernel serves a layer of a group only where it would serve
+// that layer alone (the two kernels add in different orders), so that a fused
+// call gives bit for bit what separate calls give.  The layers it serves share
+// one launch when their LDS fits, the others one launch of gemv_fused_kernel.
+template <int RTP>
+static hipError_t launch_gemv_2x8_group(const GemvLayers& layers, const void* x, int64_t in, int64_t batch,
+                                        int cus, hipStream_t stream) {
+    GemvLayers streamed = {}, rest = {};
+    for (int l = 0; l < layers.n; ++l) {
+        GemvLayers one = one_layer(layers, l);
+        deal_workgroups(one, cus);
+        if (gemv_stream_lds(one, in, batch) > 0) add_layer(streamed, layers, l);
+        else add_layer(rest, layers, l);
+    }
+    if (streamed.n > 0) {
+        deal_workgroups(streamed, cus);
+        const size_t lds = gemv_stream_lds(streamed, in, batch);
+        if (lds > 0) {
+            const hipError_t e = launch_gemv_stream(streamed, x, in, batch, lds, stream);
+            if (e != hipSuccess) return e;
+        } else {   // together they need more LDS: one launch each
+            for (int l = 0; l < streamed.n; ++l) {
+                GemvLayers one = one_layer(streamed, l);
+                deal_workgroups(one, cus);
+                const hipError_t e = launch_gemv_stream(one, x, in, batch, gemv_stream_lds(one, in, batch), stream);
+                if (e != hipSuccess) return e;
+            }
+        }
+    }
+    if (rest.n > 0) {
+        deal_workgroups(rest, cus);
+        return launch_gemv_2x8<RTP>(rest, x, (int)in, (int)batch, stream);
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_gemv_fused(int scheme, GemvLayers layers, const void* x, int64_t in,
                              int64_t batch, hipStream_t stream) {
     constexpr int RTP = 2;
     if (layers.n < 1) return hipSuccess;
-    deal_workgroups(layers, device_cu_count());
+    const int cus = device_cu_count();
+    if (scheme == kScheme2x8) return launch_gemv_2x8_group<RTP>(layers, x, in, batch, cus, stream);
+    deal_workgroups(layers, cus);
     const int n = (int)in, T = (int)batch;
-    if (scheme == kScheme2x8) {
-        const size_t lds = gemv_stream_lds(layers, in, batch);
-        if (lds > 0) return launch_gemv_stream(layers, x, in, batch, lds, stream);
-        return launch_gemv_2x8<RTP>(layers, x, n, T, stream);
-    }
     if (scheme == kScheme1x16) return launch_gemv_1x16<RTP>(layers, x, n, T, stream);
     return launch_gemv_b8<RTP>(scheme, layers, x, n, T, stream);
 }

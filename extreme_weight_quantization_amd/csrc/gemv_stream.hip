@@ -53,7 +53,7 @@ constexpr int kSRepl = 8;                                   // codebook replicas
 constexpr int kSCbBytes = 2 * kCodewords2x8 * kSRepl * 16;   // 64 KB
 constexpr int kSRing = 2;                                   // steps of codes in flight per wave
 constexpr int kSMaxT = 2;
-constexpr int kSMinSteps = 5;                               // slab steps per wave below which gemv_kernel serves
+constexpr int kSMinSteps = 2;                               // slab steps per wave below which gemv_kernel serves
 
 // LDS read of 16 bytes at a byte address of the workgroup's LDS.  The kernels
 // of this file declare no static LDS, so their dynamic LDS starts at address 0.
@@ -291,10 +291,11 @@ hipError_t launch_d(const GemvLayers& layers, const void* x, int in, int T, size
 
 // LDS bytes of the streaming product for layers whose workgroups are dealt
 // (wg_end filled), or 0 if it does not serve them: batch above 2, rows of codes
-// not 16-byte aligned, more LDS than a workgroup may hold, or fewer than about
-// five slab steps per wave (there its longer prologue, x and the ring filled
-// before the first product, costs more than the streaming saves; measured
-// crossover on the 7B and 70B shapes).
+// not 16-byte aligned, more LDS than a workgroup may hold, or a single slab step
+// per wave (there its longer prologue, x staged before the first product, costs
+// more than the streaming saves: 4096x4096 at batch 1 takes 6.0 us against 5.9
+// on gemv_kernel; from two steps on it is the faster kernel, e.g. 1024x8192 6.5
+// against 7.0 and 8192x8192 9.5 against 10.3).
 size_t gemv_stream_lds(const GemvLayers& layers, int64_t in, int64_t batch) {
     if (batch < 1 || batch > kSMaxT || in % 64 != 0 || in <= 0) return 0;
     const int G = (int)(in / kGroup), n_slab = (G + kSSlab - 1) / kSSlab;

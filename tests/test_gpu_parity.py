@@ -178,6 +178,42 @@ def test_gemv_2x8_batch_1_2_every_output(out, n_in, batch):
     assert_close_all(y, ref_full(L), f"2x8 {out}x{n_in} b{batch}")
 
 
+def _random_2x8_stream_cases(n=8, seed=29):
+    """Seeded shapes for the batch 1-2 2x8 product: rows 8000-20000, inputs 64-aligned with and
+    without a ragged last slab; all but one give a wave five or more slab steps (the streaming
+    kernel), with 2-5 row tiles per workgroup."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(8000, 20000)), int(rng.choice([8192, 8256, 12288, 12352])), int(rng.integers(1, 3)))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("out,n_in,batch", _random_2x8_stream_cases())
+def test_gemv_2x8_batch_1_2_random_shapes_every_output(out, n_in, batch):
+    L = synth.make_layer("2x8", out, n_in, batch=batch, seed=out ^ n_in)
+    assert_close_all(run_gemv(L), ref_full(L), f"2x8 {out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("outs,n_in,batch", [((9000, 5000, 13000), 8192, 1), ((12000, 700), 12288, 2)])
+def test_gemv_2x8_fused_stream_every_output(outs, n_in, batch):
+    """Fused layers on the streaming kernel (the layers' workgroups dealt by size): bit-identical to
+    separate calls, every output of every layer against the oracle."""
+    x = synth.make_activations(n_in, batch, seed=5)
+    xd = torch.from_numpy(x).cuda()
+    layers, hosts = [], []
+    for li, out in enumerate(outs):
+        L = synth.make_layer("2x8", out, n_in, batch=batch, seed=40 + li)
+        L.x = x
+        layers.append(tuple(torch.from_numpy(a).cuda() for a in (L.codes, L.codebooks, L.scales)))
+        hosts.append(L)
+    ys = E.aqlm_linear_gemv_fused(layers, xd)
+    torch.cuda.synchronize()
+    for (c, cb, sc), y, L in zip(layers, ys, hosts):
+        y_sep = E.aqlm_linear_gemv(c, cb, sc, xd)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_sep.view(torch.int16))
+        assert_close_all(y.cpu().numpy(), ref_full(L), f"fused {L.codes.shape[0]}x{n_in} b{batch}")
+
+
 @pytest.mark.parametrize("scheme", ["2x8", "1x16"])
 @pytest.mark.parametrize("batch", [3, 16])
 def test_gemv_several_passes_and_slabs(scheme, batch):
