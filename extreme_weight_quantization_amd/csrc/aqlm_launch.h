@@ -65,7 +65,7 @@ hipError_t launch_gemv(int scheme, const void* codes, const void* codebooks, con
                        const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                        hipStream_t stream);
 
-// The streaming 2x8 product for batch 1-2 (gemv_stream.hip).  gemv_stream_lds: its LDS
+// The streaming 2x8 product for batch 1-4 (gemv_stream.hip).  gemv_stream_lds: its LDS
 // bytes for layers whose workgroups are dealt, or 0 where it does not serve them.
 size_t gemv_stream_lds(const GemvLayers& layers, int64_t in, int64_t batch);
 hipError_t launch_gemv_stream(const GemvLayers& layers, const void* x, int64_t in, int64_t batch, size_t lds,

@@ -34,8 +34,9 @@
 //    together then touch 16 distinct groups.  With the 16-row x stage (128 KB)
 //    above batch 8 only 4 replicas fit.  1x16 codewords are gathered from the
 //    L2-resident 1 MiB codebook;
-//  * at batch 1-2 on layers with at least about five slab steps per wave the
-//    streaming kernel of gemv_stream.hip runs instead (gemv_stream_lds);
+//  * at batch 1-2 on layers with at least two slab steps per wave, and at
+//    batch 3-4 with at least four, the streaming kernel of gemv_stream.hip
+//    runs instead (gemv_stream_lds);
 //  * the other 2-bit schemes with B = 8 ("Key AQLM quantization parameters":
 //    1x8 g4, 4x8 g16, 8x8 g32 cost the same bits as 2x8) store in/4 code bytes
 //    per row too, so the same decomposition serves them; only the decode of a

@@ -1,4 +1,4 @@
-// Decode-phase product of the 2x8 scheme at batch 1-2 on large layers:
+// Decode-phase product of the 2x8 scheme at batch 1-4 on large layers:
 // y[b][i] = s[i] * sum_k Wc[i][k] x[b][k].
 //
 // "The AQLM Quantization Algorithm, Explained", section "Why and what do we
@@ -52,8 +52,9 @@ constexpr int kSSlab = 32;                                  // groups per slab
 constexpr int kSRepl = 8;                                   // codebook replicas
 constexpr int kSCbBytes = 2 * kCodewords2x8 * kSRepl * 16;   // 64 KB
 constexpr int kSRing = 2;                                   // steps of codes in flight per wave
-constexpr int kSMaxT = 2;
+constexpr int kSMaxT = 4;
 constexpr int kSMinSteps = 2;                               // slab steps per wave below which gemv_kernel serves
+constexpr int kSMinSteps34 = 4;                             // the same at batch 3-4 (x takes longer to stage)
 
 // LDS read of 16 bytes at a byte address of the workgroup's LDS.  The kernels
 // of this file declare no static LDS, so their dynamic LDS starts at address 0.
@@ -128,8 +129,8 @@ __device__ __forceinline__ void stream_body(const uint8_t* __restrict__ codes, c
     // this wave's tiles: local j = 0 .. mt - 1 is row tile bid + (tp + TP j) nwg
     const int mt = (wave < geo.SP * geo.TP && tp < geo.R) ? (geo.R - tp + geo.TP - 1) / geo.TP : 0;
     const int total = mt * nsl;                     // steps: tile j = k / nsl, slab sa + k % nsl
-    const int xrows = T * G;                        // 16-byte entries of x in LDS
-    const int xslots = (xrows + 63) & ~63;
+    const int XS = ((G + 63) & ~63) + 1;           // 16-byte entries a batch row of x takes in LDS (= 1 mod 16)
+    const int xslots = (T * XS + 63) & ~63;
     const int nred = geo.SP + 1;                    // partials per tile: the slab parts, then the ragged slab
     float* red = reinterpret_cast<float*>(smem + kSCbBytes / 16 + xslots);
     const uint16_t* c16 = reinterpret_cast<const uint16_t*>(codes);
@@ -165,13 +166,17 @@ __device__ __forceinline__ void stream_body(const uint8_t* __restrict__ codes, c
             (const void*)(codebooks + (size_t)((km & 1) * kCodewords2x8 + (km >> 1)) * kGroup),
             lds_ptr(smem + it * kSThreads + wave * kWave), 16, 0, 0);
     }
-    // x: entry b G + j (batch row b, group j) after the codebooks; entries past
-    // the end of a 64-entry chunk repeat the last one.
-    for (int c = wave; c * kWave < xrows; c += kSWaves) {
-        const int e = min(c * kWave + lane, xrows - 1);
-        const int b = e / G, j = e - b * G;
-        __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)b * in + (size_t)j * kGroup),
-                                         lds_ptr(smem + kSCbBytes / 16 + c * kWave), 16, 0, 0);
+    // x: entry b XS + j (batch row b, group j) after the codebooks; entries past
+    // the end of a row's last 64-entry chunk repeat its last group.  XS = 1 mod 16,
+    // so the lanes of the T batch columns that read one group of their rows
+    // together hit T distinct 16-byte bank groups.
+    {
+        const int nch = (G + kWave - 1) / kWave;   // 64-entry chunks a row
+        for (int c = wave; c < T * nch; c += kSWaves) {
+            const int b = c / nch, j = min((c - b * nch) * kWave + lane, G - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)b * in + (size_t)j * kGroup),
+                                             lds_ptr(smem + kSCbBytes / 16 + b * XS + (c - b * nch) * kWave), 16, 0, 0);
+        }
     }
     // partials start at zero (a wave with no steps leaves its slots untouched)
     for (int e = tid; e < geo.R * nred * 16 * T; e += kSThreads) red[e] = 0.f;
@@ -181,7 +186,7 @@ __device__ __forceinline__ void stream_body(const uint8_t* __restrict__ codes, c
     const uint32_t mA = (lane >> 3) & 1u, r16 = (lane & 7u) * 16u;
     const uint32_t base = (r16 + 128u * mA) | ((r16 + 128u * (mA ^ 1u)) << 8);
     const int xrow = min(lrow, T - 1);   // batch columns past the batch repeat the last row (discarded)
-    const uint32_t xlane = (uint32_t)kSCbBytes + 16u * (uint32_t)(xrow * G + 8 * kq);
+    const uint32_t xlane = (uint32_t)kSCbBytes + 16u * (uint32_t)(xrow * XS + 8 * kq);
     // lane (kq, lrow), lrow < T, holds rows 4 kq + r of batch column lrow of a tile
     auto write_partial = [&](int j, int slot, const f32x4& acc) {
         const int i = tp + geo.TP * j;
@@ -290,12 +295,15 @@ hipError_t launch_d(const GemvLayers& layers, const void* x, int in, int T, size
 }  // namespace
 
 // LDS bytes of the streaming product for layers whose workgroups are dealt
-// (wg_end filled), or 0 if it does not serve them: batch above 2, rows of codes
+// (wg_end filled), or 0 if it does not serve them: batch above 4, rows of codes
 // not 16-byte aligned, more LDS than a workgroup may hold, or a single slab step
 // per wave (there its longer prologue, x staged before the first product, costs
 // more than the streaming saves: 4096x4096 at batch 1 takes 6.0 us against 5.9
 // on gemv_kernel; from two steps on it is the faster kernel, e.g. 1024x8192 6.5
-// against 7.0 and 8192x8192 9.5 against 10.3).
+// against 7.0 and 8192x8192 9.5 against 10.3).  At batch 3-4, where x takes
+// twice as long to stage, it needs four steps a wave: 11008x4096 (three) takes
+// 9.1 us against 9.0, 8192x8192 (four) 10.0 against 10.2, 28672x8192 21.5
+// against 28.3.
 size_t gemv_stream_lds(const GemvLayers& layers, int64_t in, int64_t batch) {
     if (batch < 1 || batch > kSMaxT || in % 64 != 0 || in <= 0) return 0;
     const int G = (int)(in / kGroup), n_slab = (G + kSSlab - 1) / kSSlab;
@@ -306,8 +314,8 @@ size_t gemv_stream_lds(const GemvLayers& layers, int64_t in, int64_t batch) {
         wg0 = layers.wg_end[l];
         rmax = std::max(rmax, (n_rt + w - 1) / w);
     }
-    if ((int64_t)rmax * n_slab < kSMinSteps * kSWaves) return 0;
-    const size_t xslots = (size_t)((batch * G + 63) & ~63);
+    if ((int64_t)rmax * n_slab < (batch > 2 ? kSMinSteps34 : kSMinSteps) * kSWaves) return 0;
+    const size_t xslots = (size_t)((batch * (((G + 63) & ~63) + 1) + 63) & ~63);
     const size_t lds = (size_t)kSCbBytes + xslots * 16 + (size_t)rmax * (SP + 1) * 16 * batch * sizeof(float);
     return lds <= (size_t)160 * 1024 ? lds : 0;
 }

@@ -180,8 +180,8 @@ def test_gemv_2x8_batch_1_2_every_output(out, n_in, batch):
 
 def _random_2x8_stream_cases(n=8, seed=29):
     """Seeded shapes for the batch 1-2 2x8 product: rows 8000-20000, inputs 64-aligned with and
-    without a ragged last slab; all but one give a wave five or more slab steps (the streaming
-    kernel), with 2-5 row tiles per workgroup."""
+    without a ragged last slab; each gives a wave two or more slab steps (the streaming kernel),
+    with 2-5 row tiles per workgroup."""
     rng = np.random.default_rng(seed)
     return [(int(rng.integers(8000, 20000)), int(rng.choice([8192, 8256, 12288, 12352])), int(rng.integers(1, 3)))
             for _ in range(n)]
@@ -193,7 +193,21 @@ def test_gemv_2x8_batch_1_2_random_shapes_every_output(out, n_in, batch):
     assert_close_all(run_gemv(L), ref_full(L), f"2x8 {out}x{n_in} b{batch}")
 
 
-@pytest.mark.parametrize("outs,n_in,batch", [((9000, 5000, 13000), 8192, 1), ((12000, 700), 12288, 2)])
+@pytest.mark.parametrize("out,n_in,batch", [
+    (9000, 8192, 3),    # three row tiles a workgroup, two slabs a wave
+    (9000, 8256, 4),    # a ragged last slab at batch 4
+    (20000, 4096, 4),   # one slab a wave, five row tiles a workgroup
+    (8200, 12288, 3),   # the largest x that fits the LDS at batch 3
+])
+def test_gemv_2x8_batch_3_4_stream_every_output(out, n_in, batch):
+    """The 2x8 product at batch 3-4 on layers that give a wave four or more slab steps (the
+    streaming kernel, x rows padded apart in LDS), every output against the oracle."""
+    L = synth.make_layer("2x8", out, n_in, batch=batch, seed=out + batch)
+    assert_close_all(run_gemv(L), ref_full(L), f"2x8 {out}x{n_in} b{batch}")
+
+
+@pytest.mark.parametrize("outs,n_in,batch", [((9000, 5000, 13000), 8192, 1), ((12000, 700), 12288, 2),
+                                             ((9000, 1024, 9000), 8192, 4)])
 def test_gemv_2x8_fused_stream_every_output(outs, n_in, batch):
     """Fused layers on the streaming kernel (the layers' workgroups dealt by size): bit-identical to
     separate calls, every output of every layer against the oracle."""
