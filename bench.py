@@ -47,6 +47,11 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
 # plain (unfused) add, subtract or multiply peaks at half that op rate.
 VALU_F32_PEAK_TOPS = 157.3 / 2.0
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
+# Seconds of untimed replays before each breakdown measurement.  The GPU clock falls
+# when the device idles (host-side setup between measurements) and takes tens of
+# milliseconds of load to climb back: timed cold, a 10-launch prefill measurement
+# ran 5-10 % slower than the same launches in steady state.
+WARM_S = 0.25
 
 BLOCK_7B = ((4096, 4096),) * 4 + ((11008, 4096),) * 2 + ((4096, 11008),)
 SHAPES_7B = ((4096, 4096), (11008, 4096), (4096, 11008))
@@ -165,6 +170,16 @@ def capture(torch, launches):
     return g
 
 
+def warm(torch, graph, secs=WARM_S):
+    """Replays `graph` (untimed) until the device has been busy for `secs` seconds."""
+    t0 = time.perf_counter()
+    while True:
+        graph.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= secs:
+            return
+
+
 def replay_us(torch, graph, reps=1):
     """Wall time on the device of `reps` replays of `graph`, in microseconds (HIP events)."""
     stream = torch.cuda.current_stream()
@@ -223,33 +238,40 @@ def fused_block_launches(E, ls, k0, n_steps, lists=False):
 
 
 def time_fused_block(torch, E, ls: LayerSet, steps, warmup, lists=False):
-    """ms per 7B block step with fused projections (same rotation and graph timing as time_gemv)."""
+    """ms per 7B block step with fused projections (same rotation and graph timing as time_gemv,
+    after WARM_S seconds of untimed replays)."""
     g_warm = capture(torch, fused_block_launches(E, ls, 0, max(1, warmup), lists))
     g_main = capture(torch, fused_block_launches(E, ls, warmup, steps, lists))
     replay_us(torch, g_warm)
+    warm(torch, g_main)
     ms_step = replay_us(torch, g_main) / steps / 1e3
     del g_warm, g_main
     return ms_step
 
 
-def time_gemv(torch, E, ls: LayerSet, steps, warmup, lists=False):
+def time_gemv(torch, E, ls: LayerSet, steps, warmup, lists=False, warm_s=WARM_S):
     """Times exactly `steps` passes over the layer list (rotating buffer sets).
 
     The launches are captured in a HIP graph so that the device runs them
     back to back; the timed region is one replay of that graph between two
-    HIP events.  Per-shape kernel durations come from graphs of back-to-back
-    launches of one shape.  Returns (ms per step, {shape: us per launch}).
+    HIP events, after one replay of `warmup` steps and `warm_s` seconds of
+    untimed replays of the timed graph (0 for the headline: exactly `warmup`
+    steps).  Per-shape kernel durations come from graphs of back-to-back
+    launches of one shape, each after WARM_S seconds of untimed replays.
+    Returns (ms per step, {shape: us per launch}).
     """
     g_warm = capture(torch, gemv_launches(E, ls, 0, max(1, warmup), lists=lists))
     g_main = capture(torch, gemv_launches(E, ls, warmup, steps, lists=lists))
     replay_us(torch, g_warm)
+    if warm_s > 0:
+        warm(torch, g_main, warm_s)
     ms_step = replay_us(torch, g_main) / steps / 1e3
     per_shape = {}
     for shape in dict.fromkeys(ls.shapes):
         n = max(1, min(len(ls.sets), 64))
         g = capture(torch, gemv_launches(E, ls, 0, n, only=shape, lists=lists))
         count = n * ls.shapes.count(shape)
-        replay_us(torch, g)
+        warm(torch, g)
         per_shape[shape] = replay_us(torch, g, reps=4) / (4 * count)
         del g
     del g_warm, g_main
@@ -276,11 +298,12 @@ def hbm_copy_gbps(torch, mib=512, reps=10):
 
 
 def time_calls(torch, launch, iters, warmup):
-    """Mean us per launch of `launch(i)` over `iters` back-to-back launches in a HIP graph."""
+    """Mean us per launch of `launch(i)` over `iters` back-to-back launches in a HIP graph
+    (after `warmup` eager launches and WARM_S seconds of untimed replays)."""
     for i in range(warmup):
         launch(i)
     g = capture(torch, [lambda i=i: launch(i) for i in range(iters)])
-    replay_us(torch, g)
+    warm(torch, g)
     us = replay_us(torch, g, reps=3) / (3 * iters)
     del g
     return us
@@ -410,7 +433,7 @@ def main():
     entry_bytes_step = ls.pack_lists(torch, E)
     worst = spot_check(torch, E, ls, lists=True)
     torch.cuda.synchronize()
-    ms_step, shape_us = time_gemv(torch, E, ls, args.steps, args.warmup, lists=True)
+    ms_step, shape_us = time_gemv(torch, E, ls, args.steps, args.warmup, lists=True, warm_s=0)
     value = ls.bytes_per_step / (ms_step * 1e-3) / 1e9
     kern_us_step = sum(shape_us[sh] for sh in BLOCK_7B)
     achieved = ls.bytes_per_step / (kern_us_step * 1e-6) / 1e9

@@ -11,16 +11,22 @@
 // each weight once.
 //
 // A workgroup owns a 256-token x 128-row output tile and walks k in steps of
-// 64 inputs, each split into two k-halves of 32 for the products.  Eight waves
-// each own a 64x64 piece: they copy their share of the X and W tiles of a step
-// straight from global memory into LDS (direct-to-LDS loads), read 16-byte
-// fragments and run 16x16x32 fp16 matrix-core products with fp32 accumulators.
+// 64 inputs, each split into two k-halves of 32 for the products.  Twelve
+// waves play two roles:
+//   8 consumer waves  each own a 64x64 piece: they read 16-byte fragments from
+//                     LDS and run 16x16x32 fp16 matrix-core products with fp32
+//                     accumulators, and issue no global load;
+//   4 loader waves    copy the X and W tiles of each step straight from global
+//                     memory into LDS (direct-to-LDS loads), 12 loads a wave.
+// With the copies in the consumer waves instead (6 loads each) the product took
+// 10-13 % longer; with two loader waves, 6-9 % longer.
 //
 // Pipeline (one barrier per step; B_k is the barrier that ends step k):
-//   step k : load the X and W tiles of step k+2 (whole rows of 128 bytes);
-//            read half 0 of step k while multiplying half 1 of step k-1;
-//            read half 1 of step k while multiplying half 0 of step k;
-//            B_k waits for every load issued before step k.
+//   step k : loaders load the X and W tiles of step k+2 (whole rows of 128
+//            bytes); consumers read half 0 of step k while multiplying half 1
+//            of step k-1, then read half 1 of step k while multiplying half 0;
+//            B_k: the loaders' loads issued before step k have landed and the
+//            consumers' fragment reads are done.
 // X and W keep three whole-step stages each: 96 + 48 = 144 KB of LDS.  The
 // products run in the same order as a plain k loop, so the skew changes no
 // result.
@@ -33,7 +39,7 @@
 // fragment read (16 consecutive rows, one chunk) hit 16 distinct 16-byte bank
 // groups.
 //
-// Epilogue (out % 8 == 0): after a last barrier each wave passes its 64x64 tile
+// Epilogue (out % 8 == 0): after a last barrier each consumer wave passes its 64x64 tile
 // through LDS and stores whole 128-byte rows of y, 16 bytes per lane.
 //
 // Tile order: consecutive workgroups go to different XCDs, so workgroup b
@@ -49,8 +55,9 @@ namespace {
 
 constexpr int kDenseBM = 256;                // tokens per tile
 constexpr int kDenseBN = 128;                // output rows per tile
-constexpr int kDenseWaves = 8;
-constexpr int kDenseThreads = 64 * kDenseWaves;
+constexpr int kDenseWaves = 8;                // consumer waves: the products
+constexpr int kDenseLoaders = 4;              // loader waves: the global-to-LDS copies
+constexpr int kDenseThreads = 64 * (kDenseWaves + kDenseLoaders);
 constexpr int kDenseXStage = kDenseBM * 8;   // 16-byte slots of one X stage (a whole 64-input step)
 constexpr int kDenseWStage = kDenseBN * 8;   // 16-byte slots of one W stage
 constexpr int kDenseStages = 3;
@@ -59,8 +66,8 @@ constexpr size_t kDenseLds = (size_t)(kDenseWOff + kDenseStages * kDenseWStage) 
 static_assert(kDenseLds <= 163840, "LDS budget");
 constexpr int kXcds = 8;                     // tile order only; any count gives correct results
 
-// loads a wave issues per step: 4 of X (32 rows), 2 of W (16 rows)
-constexpr int kDenseLoadsPerStep = 6;
+// loads a loader wave issues per step: 8 of X (64 rows), 4 of W (32 rows)
+constexpr int kDenseLoadsPerStep = 12;
 
 __device__ __forceinline__ int stage_slot(int r, int c) { return 8 * r + (c ^ ((r >> 1) & 7)); }
 
@@ -83,7 +90,8 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
     u32x4* Ws = smem + kDenseWOff;    // [stage 3][kDenseWStage]
     const int tile = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
     if (tile >= n_tiles) return;      // the whole workgroup: the grid is rounded up to kXcds * per_xcd
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lw = wave - kDenseWaves;   // loader index (loader waves only)
     const int n0 = (tile / n_tt) * kDenseBN;
     const int t0 = (tile % n_tt) * kDenseBM;
     const int n_k = in / 64;          // the launcher guarantees in % 64 == 0
@@ -97,8 +105,8 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
         u32x4* dx = Xs + (j % kDenseStages) * kDenseXStage;
         u32x4* dw = Ws + (j % kDenseStages) * kDenseWStage;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = 4 * wave + i;
+        for (int i = 0; i < 8; ++i) {
+            const int q = 8 * lw + i;
             const int r = 8 * q + rsub;
             const int c = (lane & 7) ^ ((r >> 1) & 7);
             const int tok = min(t0 + r, T - 1);
@@ -106,8 +114,8 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
                                              lds_ptr(dx + 64 * q), 16, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = 2 * wave + i;
+        for (int i = 0; i < 4; ++i) {
+            const int q = 4 * lw + i;
             const int r = 8 * q + rsub;
             const int c = (lane & 7) ^ ((r >> 1) & 7);
             const int row = min(n0 + r, out - 1);
@@ -146,15 +154,33 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix product
         }
     };
-    load_step(0);
-    load_step(1);
+    if (lw >= 0) {
+        // loader: the same barriers as the consumers, the loads of step k+2 after B_{k-1}
+        // (stage (k-1) % 3: step k-1 was read before B_{k-1})
+        load_step(0);
+        load_step(1);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // steps 0 and 1 landed
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        load_step(2);
+        for (int k = 1; k < n_k; ++k) {
+            step_barrier();
+            load_step(k + 2);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // no load in flight into the epilogue's LDS
+        if (out % 8 == 0) {
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+        return;
+    }
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));   // steps 0 and 1 landed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     f16x8 a0[4], b0[4], a1[4], b1[4];
     // step 0: both halves of stage 0 read, half 0 multiplied
-    load_step(2);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(0, 0, a0, b0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -162,7 +188,6 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(const f16* __
     mma16(a0, b0);
     for (int k = 1; k < n_k; ++k) {
         step_barrier();
-        load_step(k + 2);       // stage (k-1) % 3: step k-1 was read before B_{k-1}
         __builtin_amdgcn_sched_barrier(0);
         read_frags(k, 0, a0, b0);
         mma16(a1, b1);          // half 1 of step k-1
