@@ -341,6 +341,8 @@ def run_fused(layers, x):
     ((100, 4096, 37, 1000), 520, 3),      # ragged rows and in, uneven layers
     ((100, 4096, 37, 1000), 576, 1),      # ragged rows and last slab, 64-aligned in
     ((28672, 28672), 8192, 2),            # 70B gate, up: 14 row tiles per workgroup
+    ((28672, 28672), 8192, 4),            # the same at batch 4: streamed, one launch per layer (LDS)
+    ((8192, 1024, 1024), 8192, 3),        # 70B q, k, v at batch 3: q streamed, k and v not
     ((16,) * 8, 256, 1),                  # the most layers one call takes
 ])
 def test_gemv_fused_matches_separate_and_oracle(scheme, outs, n_in, batch):
