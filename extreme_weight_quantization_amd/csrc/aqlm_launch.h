@@ -79,6 +79,10 @@ hipError_t launch_gemm_pipe_2x8(const void* codes, const void* codebooks, const 
 hipError_t launch_gemm_pipe_1x8g4(const void* codes, const void* codebooks, const void* scales,
                                   const void* x, void* y, int64_t out, int64_t in, int64_t batch,
                                   hipStream_t stream);
+// And for 1x16 (16-bit codes, codewords gathered from L2 by producer waves of their own); in % 64 == 0.
+hipError_t launch_gemm_pipe_1x16(const void* codes, const void* codebooks, const void* scales,
+                                 const void* x, void* y, int64_t out, int64_t in, int64_t batch,
+                                 hipStream_t stream);
 // And for 4x8 g16 (4 code bytes per 16 inputs, also 2 bytes per 8 at the same places); in % 64 == 0.
 hipError_t launch_gemm_pipe_4x8g16(const void* codes, const void* codebooks, const void* scales,
                                    const void* x, void* y, int64_t out, int64_t in, int64_t batch,

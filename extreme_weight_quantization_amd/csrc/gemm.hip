@@ -19,8 +19,8 @@
 // Consecutive workgroups take consecutive token tiles of one W tile, so with
 // 8 token tiles every XCD keeps one X tile in its L2.
 //
-// This is the general kernel (any in % 8 == 0, both schemes).  The 2x8 scheme
-// with in % 64 == 0 takes the role-split pipeline of gemm_pipe.hip instead.
+// This is the general kernel (any in % 8 == 0, both schemes).  Both schemes
+// with in % 64 == 0 take the role-split pipeline of gemm_pipe.hip instead.
 #include "aqlm_device.h"
 #include "aqlm_launch.h"
 
@@ -253,6 +253,7 @@ hipError_t launch_gemm(int scheme, const void* codes, const void* codebooks, con
             return launch_gemm_pipe_2x8(codes, codebooks, scales, x, y, out, in, batch, stream);
         return launch_gemm_t<kScheme2x8, 256, 128, 4, 2, 2>(codes, codebooks, scales, x, y, out, in, batch, stream);
     }
+    if (in % 64 == 0) return launch_gemm_pipe_1x16(codes, codebooks, scales, x, y, out, in, batch, stream);
     return launch_gemm_t<kScheme1x16, 256, 128, 4, 2, 1>(codes, codebooks, scales, x, y, out, in, batch, stream);
 }
 
