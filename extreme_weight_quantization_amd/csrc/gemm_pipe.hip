@@ -30,10 +30,12 @@
 // run kRing steps ahead; the consumers' counter only holds X loads.  Both
 // counters retire in issue order, which is why the two kinds of loads live in
 // different waves.  For 1x16 the producers split once more: two waves stream the
-// codes and two gather the codewords (8 a lane a step) and write W, so that
-// waiting for a gather never waits for code loads issued after it (1x16 at
-// 2048 tokens: 7-9 % faster than the general kernel; with the code loads moved
-// to the consumers and four gathering waves, 2-4 %).
+// codes (kept three steps ahead of the gathers) and two gather the codewords (8 a
+// lane a step) one step before they write them to W, so that waiting for a gather
+// never waits for code loads issued after it.  At 2048 tokens this is 15-17 %
+// faster than the general kernel; gathering in the step that writes, 7-9 %;
+// gathering two steps ahead, 13-15 %; the code loads moved to the consumers with
+// four gathering waves, 2-4 %.
 //
 // Pipeline (one barrier per step; B_k is the barrier that ends step k):
 //   consumer step k : load the X tile of step k+2 (whole 128-byte rows);
@@ -203,9 +205,9 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
         if constexpr (SCHEME == kScheme1x16) {
             // The 65536-entry codebook stays in L2.  Two of the producer waves stream the codes
             // into the ring (4 loads of 256 bytes each a step); the other two gather each row's 8
-            // codewords of a step from L2 and write the W tile.  Each wave's vector-memory
-            // counter then holds one kind of load, so the gathers are waited for without
-            // waiting for the code loads issued after them.
+            // codewords of a step from L2, one step before writing them to the W tile.  Each
+            // wave's vector-memory counter then holds one kind of load, so the gathers are
+            // waited for without waiting for the code loads issued after them.
             if (pw < 2) {
                 auto load_ring = [&](int j) {
                     const int jc = min(j, n_k - 1);
@@ -220,41 +222,57 @@ __global__ __launch_bounds__(kPipeThreads) void gemm_pipe_2x8_kernel(
                 };
 #pragma unroll
                 for (int j = 0; j < kPipeRing; ++j) load_ring(j);
-                // P1: codes of step 0 landed
-                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(4 * (kPipeRing - 1)) : "memory");
-                // P2: codes of step 1 landed
+                // P1: codes of steps 0 and 1 landed
                 asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(4 * (kPipeRing - 2)) : "memory");
+                // P2: codes of step 2 landed
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(4 * (kPipeRing - 3)) : "memory");
                 for (int k = 0; k + 1 < n_k; ++k) {
-                    load_ring(k + kPipeRing);   // replaces step k's codes, gathered before B_{k-1}
-                    // B_k: codes of step k+2 landed
-                    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(4 * (kPipeRing - 2)) : "memory");
+                    load_ring(k + kPipeRing);   // replaces step k's codes, gathered before B_{k-2}
+                    // B_k: codes of step k+3 landed
+                    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(4 * (kPipeRing - 3)) : "memory");
                 }
             } else {
                 const int gr = (pw - 2) * 64 + lane;   // the W row this lane writes
-                auto decode = [&](int j) {
-                    const u32x4 cv = ring[(j % kPipeRing) * kPipeBN + gr];
-                    u32x4 e[8];
+                // the codewords of a step are gathered one step before they are written
+                const f16* cbl = codebooks;
+                asm volatile("" : "+s"(cbl));   // loads through a laundered pointer stay where they are written
+                auto gather = [&](int j, u32x4 (&e)[8]) {
+                    const u32x4 cv = ring[(min(j, n_k - 1) % kPipeRing) * kPipeBN + gr];
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
                         const uint32_t code = (cv[q >> 1] >> (16 * (q & 1))) & 0xffffu;
-                        e[q] = load16(codebooks + (size_t)code * kGroup);
+                        e[q] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(
+                            (uintptr_t)(cbl + (size_t)code * kGroup));
                     }
+                };
+                auto write = [&](int j, const u32x4 (&e)[8]) {
                     u32x4* d = Ws + (j % kPipeWStages) * kPipeWStage;
 #pragma unroll
                     for (int q = 0; q < 8; ++q) d[stage_slot(gr, q)] = e[q];
                 };
-                // P1: codes of step 0 landed (the ring waves' side)
+                u32x4 ea[8], eb[8];
+                // P1: codes of steps 0 and 1 landed (the ring waves' side)
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                 __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-                decode(0);
-                // P2: W(0) written
-                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                gather(0, ea);
+                gather(1, eb);
+                write(0, ea);
+                // P2: W(0) written; codes of step 2 landed
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                 __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-                for (int k = 0; k + 1 < n_k; ++k) {
-                    decode(k + 1);   // stage (k+1) % 2: step k-1's W was read before B_{k-1}
-                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                // step k: gather step k+2 (its codes landed at B_{k-1}), write step k+1
+                auto round = [&](int k, u32x4 (&next)[8], u32x4 (&cur)[8]) {
+                    gather(k + 2, next);
+                    write(k + 1, cur);   // stage (k+1) % 2: step k-1's W was read before B_{k-1}
+                    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                };
+                int k = 0;
+                for (; k + 2 < n_k; k += 2) {   // both register sets every round
+                    round(k, ea, eb);
+                    round(k + 1, eb, ea);
                 }
+                if (k + 1 < n_k) round(k, ea, eb);
             }
             if (out % 8 == 0) {
                 asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
