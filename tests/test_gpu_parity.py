@@ -388,7 +388,9 @@ def run_gemm(layer):
     (128, 256, 256),
     (17, 8, 3),
     (200, 64, 70),      # a single k-step
-    (1000, 1024, 513),  # 2x8 pipelined path: several row and token tiles, ragged
+    (1000, 1024, 513),  # pipelined path: several row and token tiles, ragged
+    (129, 64, 257),     # pipelined path: one k-step, rows not a multiple of 8, a second token tile
+    (70, 1088, 300),    # pipelined path: 17 k-steps (the code ring wraps), ragged rows and tokens
 ])
 def test_gemm_small(scheme, out, n_in, batch):
     L = synth.make_layer(scheme, out, n_in, batch=batch, seed=0)
