@@ -80,8 +80,14 @@ constexpr int kRedStride = kRowTile * kRedRow;
 // The operand layout puts a different batch row in each of 16 consecutive
 // lanes, so a direct load looks up one cache line per active lane; the staged
 // load looks up one per four lanes.
-enum XMode : int { kXDirect = 0, kXStaged8 = 1, kXStaged16 = 2 };
-constexpr int kXStageSlots(int xm) { return xm == kXStaged16 ? 16 * kSlabGroups : xm == kXStaged8 ? 8 * kSlabGroups : 0; }
+//   kXStaged16in8 16 batch rows through an 8-row stage, in two halves: rows 0-7,
+//                 read into the operand layout, then rows 8-15 into the same slots.
+//                 Half the LDS of the 16-row stage, so the 2x8 codebooks keep 8
+//                 replicas above batch 8, for one more load round trip per slab.
+enum XMode : int { kXDirect = 0, kXStaged8 = 1, kXStaged16 = 2, kXStaged16in8 = 3 };
+constexpr int kXStageSlots(int xm) {
+    return xm == kXStaged16 ? 16 * kSlabGroups : (xm == kXStaged8 || xm == kXStaged16in8) ? 8 * kSlabGroups : 0;
+}
 
 // Loads the 8 two-byte codes of a lane's chunk (row, groups g0 .. g0+7),
 // packed two per 32-bit word.  The load is unconditional, with the row and
@@ -239,7 +245,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
                                           const f16* __restrict__ scales, f16* __restrict__ y, const int out,
                                           const int bid, const int nwg, const f16* __restrict__ x, int in, int T) {
 
-    constexpr bool XS = XM == kXStaged8 || XM == kXStaged16;
+    constexpr bool XS = XM == kXStaged8 || XM == kXStaged16 || XM == kXStaged16in8;
     constexpr int kStage = kXStageSlots(XM);    // 16-byte slots of one wave's x stage
     constexpr int kStageRows = kStage / kSlabGroups;
     extern __shared__ u32x4 smem[];
@@ -290,7 +296,9 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
     // column depends on its own B column only, and the columns past the batch
     // are discarded; groups past the matrix are zeroed when read.
     u32x4* const xst = smem + kCbSlots + (XS ? wave * kStage : 0);
-    auto stage_x = [&](int s) {
+    // Batch rows r0 .. r0 + kStageRows - 1 of slab s into the stage (stage row b holds
+    // batch row r0 + b).
+    auto stage_rows = [&](int s, int r0) {
         // The lane index passes through an empty asm statement so that the
         // address arithmetic stays here instead of being hoisted out of the
         // loops as eight live 64-bit pointers.
@@ -298,13 +306,15 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
         asm volatile("" : "+v"(l));
 #pragma unroll
         for (int i = 0; i < kStageRows / 2; ++i) {
-            if (2 * i >= T) break;   // rows past the batch only feed discarded columns
+            if (r0 + 2 * i >= T) break;   // rows past the batch only feed discarded columns
             const int b = 2 * i + (l >> 5);
             const int grp = min(s * kSlabGroups + ((l & 31) ^ b), G - 1);
-            __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)min(b, T - 1) * in + (size_t)grp * kGroup),
-                                             lds_ptr(xst + 64 * i), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(x + (size_t)min(r0 + b, T - 1) * in + (size_t)grp * kGroup),
+                lds_ptr(xst + 64 * i), 16, 0, 0);
         }
     };
+    auto stage_x = [&](int s) { stage_rows(s, 0); };
     // Waits for every load of this wave (the stage among them), reads the operand
     // layout; groups past the end of the row read as zero so that their
     // products stay zero whatever x holds.
@@ -322,6 +332,25 @@ __device__ __forceinline__ void gemv_body(const uint8_t* __restrict__ codes, con
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the stage is free again
         asm volatile("" ::: "memory");
+        if constexpr (XM == kXStaged16in8) {
+            // the second half: rows 8-15 into the same slots, read by the lanes of
+            // operand columns 8-15
+            if (T > kStageRows) {
+                __builtin_amdgcn_sched_barrier(0);
+                stage_rows(s, kStageRows);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int c = slab_group(kq, q);
+                    const f16x8 v = as_f16x8(xst[kSlabGroups * b + (c ^ b)]);
+                    if (lrow >= kStageRows) bx[q] = (s * kSlabGroups + c < G) ? v : f16x8{};
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the stage is free again
+                asm volatile("" ::: "memory");
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
     int s_loaded = -1;   // slab whose activations are in bx
@@ -552,15 +581,16 @@ static hipError_t launch_gemv_v(const GemvLayers& layers, const void* x, int n, 
 // Up to this batch the 2x8 product loads x directly (a few active lanes per
 // load); above it x is staged.
 constexpr int kGemvDirectBatch2x8 = 2;
-// Above this batch the stage holds 16 rows; the 2x8 codebooks then keep 4
-// replicas instead of 8 (LDS: 32 + 128 KB).
+// Above this batch 16 rows are staged: for 2x8 in two halves through an 8-row
+// stage, so that the codebooks keep 8 replicas (LDS: 64 + 64 KB; with a 16-row
+// stage only 4 fit, and their lookups met 2-way bank conflicts).
 constexpr int kGemvStage8Batch = 8;
 
 template <int RTP>
 static hipError_t launch_gemv_2x8(const GemvLayers& layers, const void* x, int n, int T, hipStream_t stream) {
     if (T <= kGemvDirectBatch2x8) return launch_gemv_v<kScheme2x8, 8, RTP, kXDirect>(layers, x, n, T, stream);
     if (T <= kGemvStage8Batch) return launch_gemv_v<kScheme2x8, 8, RTP, kXStaged8>(layers, x, n, T, stream);
-    return launch_gemv_v<kScheme2x8, 4, RTP, kXStaged16>(layers, x, n, T, stream);
+    return launch_gemv_v<kScheme2x8, 8, RTP, kXStaged16in8>(layers, x, n, T, stream);
 }
 
 // The other 2-bit B = 8 schemes: as 2x8, with the replicas that fit next to the x stage.
